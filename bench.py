@@ -1,0 +1,342 @@
+"""Benchmark of the batch-invariant hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of M = 4096 synthetic rows
+at Llama-3-8B projection shapes (K = 4096):
+    H  = bi_rmsnorm(X, g)                      X [M, 4096] ~ N(0,1), g ~ N(1, 0.1^2)
+    Q  = bi_gemm(H, Wq)     N = 4096            W* ~ N(0, 0.02^2), stored [N, K]
+    KV = bi_gemm(H, Wkv)    N = 1024
+    U  = bi_gemm(H, Wup)    N = 14336
+    D  = bi_gemm(U, Wdown)  K = 14336, N = 4096
+    L  = bi_lora_shrink(H, A, split 8)   and the unsplit pass and the atomic
+         control (A [16, 4096] ~ N(0, 0.01^2), fp32 out)
+    bi_row_bitdiff: probe rows of Q and D against the same rows computed alone
+Inputs are resident in HBM before timing starts.  ``value`` is the step's
+algorithmic TFLOP/s (2*M*N*K per GEMM, 2*M*R*K per shrink) over the timed
+steps.  ``roofline`` is for the dominant kernel (the 256x256-tile GEMM, which
+runs Q, U and D), timed with HIP events around its launches on the launch
+stream.  ``cpu_baseline`` is the fp64 CPU oracle timed on a bounded row sample
+of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--M 4096]
+       [--sweep FILE]   also time each kernel over an M sweep (JSONL to FILE)
+       [--only NAME]    run only one kernel repeatedly (for rocprofv3 counters)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "batch-invariant bf16 GEMM TFLOP/s (% MFMA peak) over M; RMSNorm GB/s (% HBM)"
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+K_MODEL, N_Q, N_KV, N_UP = 4096, 4096, 1024, 14336
+R_LORA = 16
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--M", type=int, default=4096)
+    ap.add_argument("--sweep", default=None)
+    ap.add_argument("--only", default=None,
+                    choices=["gemm", "gemm_kv", "rmsnorm", "shrink_det8", "shrink_atomic8",
+                             "shrink_unsplit", "copy"])
+    ap.add_argument("--iters", type=int, default=50, help="launches for --only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "this path has no multi-GPU mode; row sharding needs no exchange and is "
+              "described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from invariant_deterministic_amd import binding as bi
+    from invariant_deterministic_amd import synth, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M = args.M
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t0 = time.time()
+    x = workloads.llama8b_x(K_MODEL, rows=M)
+    g = synth.normal_bf16((K_MODEL,), 2002, mean=1.0, std=0.1)
+    ws_h = [workloads.llama8b_w(i) for i in range(4)]
+    a = workloads.lora_inputs(1)[1]
+    X, G, A = to_dev(x), to_dev(g), to_dev(a)
+    Wq, Wkv, Wup, Wdown = (to_dev(w) for w in ws_h)
+    H = torch.empty((M, K_MODEL), dtype=torch.bfloat16, device=dev)
+    Q = torch.empty((M, N_Q), dtype=torch.bfloat16, device=dev)
+    KV = torch.empty((M, N_KV), dtype=torch.bfloat16, device=dev)
+    U = torch.empty((M, N_UP), dtype=torch.bfloat16, device=dev)
+    D = torch.empty((M, K_MODEL), dtype=torch.bfloat16, device=dev)
+    L = torch.empty((M, R_LORA), dtype=torch.float32, device=dev)
+    Lu = torch.empty_like(L)
+    La = torch.empty_like(L)
+    WS = torch.empty(bi.bi_lora_shrink_workspace_bytes(M, R_LORA, 8), dtype=torch.uint8, device=dev)
+    eps = workloads.EPS
+    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    if args.only:
+        run_only(args, bi, torch, dev, X, G, H, Wq, Wkv, U, A, L, WS, La, Lu, eps)
+        return
+
+    # Probe rows: each computed alone through the whole chain, for the in-step
+    # bitwise check.
+    probes = sorted({0, 1, 255, 256, M // 2, M - 1} & set(range(M)))
+    solo_q = torch.empty((len(probes), N_Q), dtype=torch.bfloat16, device=dev)
+    solo_d = torch.empty((len(probes), K_MODEL), dtype=torch.bfloat16, device=dev)
+    for i, p in enumerate(probes):
+        h1 = bi.bi_rmsnorm(X[p:p + 1], G, eps=eps)
+        bi.bi_gemm(h1, Wq, y=solo_q[i:i + 1])
+        u1 = bi.bi_gemm(h1, Wup)
+        bi.bi_gemm(u1, Wdown, y=solo_d[i:i + 1])
+    probe_pos = torch.tensor(probes, dtype=torch.int64, device=dev)
+    probe_ids = torch.arange(len(probes), dtype=torch.int64, device=dev)
+    counts_q = torch.zeros((len(probes), 2), dtype=torch.int64, device=dev)
+    counts_d = torch.zeros((len(probes), 2), dtype=torch.int64, device=dev)
+
+    ev_pairs = []
+
+    def step(timed: bool):
+        bi.bi_rmsnorm(X, G, y=H, eps=eps)
+        for w, y, inp in ((Wq, Q, H), (Wkv, KV, H), (Wup, U, H), (Wdown, D, U)):
+            big = w.shape[0] >= 4096
+            if timed and big:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            bi.bi_gemm(inp, w, y=y)
+            if timed and big:
+                e1.record()
+                ev_pairs.append((e0, e1, 2.0 * M * w.shape[0] * w.shape[1]))
+        bi.bi_lora_shrink(H, A, y=L, split_k=8, ws=WS)
+        bi.bi_lora_shrink(H, A, y=Lu, split_k=1)
+        bi.bi_lora_shrink_atomic(H, A, y=La, split_k=8)
+        bi.bi_row_bitdiff(Q, solo_q, probe_pos, probe_ids, counts=counts_q, check_rows=False)
+        bi.bi_row_bitdiff(D, solo_d, probe_pos, probe_ids, counts=counts_d, check_rows=False)
+
+    # Gate before timing: the path must be batch-invariant on this input.
+    step(False)
+    torch.cuda.synchronize()
+    gate_bits = int(counts_q[:, 0].sum()) + int(counts_d[:, 0].sum())
+    if gate_bits:
+        print(json.dumps({"error": "batch-invariance gate failed", "diff_bits": gate_bits}))
+        sys.exit(1)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step(True)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+
+    flop_gemm = 2.0 * M * (K_MODEL * (N_Q + N_KV + N_UP) + N_UP * K_MODEL)
+    flop_shrink = 3 * 2.0 * M * R_LORA * K_MODEL
+    value = (flop_gemm + flop_shrink) / (ms_step * 1e-3) / 1e12
+
+    durs = [e0.elapsed_time(e1) for e0, e1, _ in ev_pairs]
+    flops = [f for _, _, f in ev_pairs]
+    avg_ms = sum(durs) / len(durs)
+    avg_flop = sum(flops) / len(flops)
+    achieved = avg_flop / (avg_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "kernel": "gemm_kernel<256,256> (Q, U, D projections)",
+                "avg_launch_us": round(avg_ms * 1e3, 2),
+                "flop_per_launch": avg_flop}
+
+    bits_after = int(counts_q[:, 0].sum()) + int(counts_d[:, 0].sum())
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3_8b_projections_step", "M": M, "K": K_MODEL,
+                   "N": [N_Q, N_KV, N_UP], "down_proj": [N_UP, K_MODEL], "lora_rank": R_LORA,
+                   "lora_split_k": 8, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "invariance": {"probe_rows": len(probes), "diff_bits_last_step": bits_after},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, g, ws_h, a, eps)
+    if args.sweep:
+        out["sweep_file"] = args.sweep
+        sweep(args.sweep, bi, torch, dev, to_dev)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(x, g, ws_h, a, eps):
+    """The oracle as it stands, on a bounded sample of one step: 16 rows through
+    RMSNorm, the four projections and the shrink (about 4.4 GFLOP of fp64)."""
+    import numpy as np
+
+    import oracle
+    rows = 16
+    xs = x[:rows]
+    t = time.perf_counter()
+    h = oracle.rmsnorm(xs, g, eps)
+    hb = oracle.bf16_round(h)
+    flop = 0.0
+    for i, w in enumerate(ws_h[:3]):
+        oracle.gemm(hb, w)
+        flop += 2.0 * rows * w.shape[0] * w.shape[1]
+    u = oracle.bf16_round(oracle.gemm(hb, ws_h[2]))
+    flop += 2.0 * rows * ws_h[2].shape[0] * ws_h[2].shape[1]
+    oracle.gemm(u, ws_h[3])
+    flop += 2.0 * rows * ws_h[3].shape[0] * ws_h[3].shape[1]
+    oracle.lora_shrink(hb, a)
+    flop += 2.0 * rows * a.shape[0] * a.shape[1]
+    sec = time.perf_counter() - t
+    return {"value": round(flop / sec / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "seconds": round(sec, 2),
+            "sample": f"{rows} rows of the step (RMSNorm, Q/KV/Up/Down projections, LoRA shrink), "
+                      f"fp64, {flop / 1e9:.1f} GFLOP; Up computed twice (timed as in the step "
+                      "and again to feed Down)"}
+
+
+def _time_loop(torch, fn, n, reps=7):
+    """Median over reps of (n launches) / n, in ms, with HIP events."""
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / n)
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def sweep(path, bi, torch, dev, to_dev):
+    """Per-kernel throughput over M, each kernel alone; inputs rotate through
+    >= 1 GiB of copies so the 256 MB last-level cache cannot serve them."""
+    import numpy as np
+
+    from invariant_deterministic_amd import synth, workloads
+    recs = []
+    GiB = 1 << 30
+
+    def copies(nbytes):
+        return max(1, min(64, -(-GiB // max(1, nbytes))))
+
+    # GEMM over M for each projection shape
+    for si, (K, N) in enumerate(workloads.LLAMA8B["shapes"]):
+        W = to_dev(workloads.llama8b_w(si))
+        xpool = to_dev(workloads.llama8b_x(K))
+        for M in (1, 16, 128, 512, 1024, 2048, 4096, 8192):
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            n = 20 if M >= 2048 else 50
+            ms = _time_loop(torch, lambda i: bi.bi_gemm(xpool[:M], W, y=y), n)
+            fl = 2.0 * M * N * K
+            by = 2.0 * (M * K + N * K + M * N)
+            t_roof = max(fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
+            recs.append({"kernel": "bi_gemm", "K": K, "N": N, "M": M, "us": ms * 1e3,
+                         "tflops": fl / (ms * 1e-3) / 1e12, "gbs": by / (ms * 1e-3) / 1e9,
+                         "frac_mfma": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "frac_roofline": t_roof / (ms * 1e-3),
+                         "config": bi.bi_gemm_config_id(N, K)})
+            print(f"# sweep gemm K={K} N={N} M={M}: {recs[-1]['tflops']:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+        del W, xpool
+    # RMSNorm over M (K = 4096), rotating buffers
+    K = 4096
+    wv = to_dev(synth.normal_bf16((K,), 2002, mean=1.0, std=0.1))
+    for M in (1, 7, 128, 2048, 8192):
+        per = 4 * M * K
+        c = copies(per)
+        xs = [torch.randn((M, K), device=dev).to(torch.bfloat16) for _ in range(c)]
+        ys = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(c)]
+        ms = _time_loop(torch, lambda i: bi.bi_rmsnorm(xs[i % c], wv, y=ys[i % c]), 4 * c)
+        by = 4.0 * M * K + 2 * K
+        recs.append({"kernel": "bi_rmsnorm", "K": K, "M": M, "us": ms * 1e3,
+                     "gbs": by / (ms * 1e-3) / 1e9, "frac_hbm": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "rotating_copies": c})
+        print(f"# sweep rmsnorm M={M}: {recs[-1]['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+        del xs, ys
+    # LoRA shrink over M, three variants, rotating buffers
+    a = to_dev(workloads.lora_inputs(1)[1])
+    for M in (1, 8, 64, 512, 4096):
+        per = 2 * M * 4096
+        c = copies(per)
+        xs = [torch.randn((M, 4096), device=dev).to(torch.bfloat16) for _ in range(c)]
+        y = torch.empty((M, 16), dtype=torch.float32, device=dev)
+        ws = torch.empty(bi.bi_lora_shrink_workspace_bytes(M, 16, 8), dtype=torch.uint8, device=dev)
+        by = 2.0 * M * 4096 + 2 * 16 * 4096 + 4 * M * 16
+        res = {}
+        for name, fn in (("det8", lambda i: bi.bi_lora_shrink(xs[i % c], a, y=y, split_k=8, ws=ws)),
+                         ("unsplit", lambda i: bi.bi_lora_shrink(xs[i % c], a, y=y, split_k=1)),
+                         ("atomic8", lambda i: bi.bi_lora_shrink_atomic(xs[i % c], a, y=y, split_k=8))):
+            ms = _time_loop(torch, fn, 4 * c)
+            res[name] = ms
+            recs.append({"kernel": f"bi_lora_shrink_{name}", "M": M, "us": ms * 1e3,
+                         "gbs": by / (ms * 1e-3) / 1e9, "frac_hbm": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "rotating_copies": c})
+        recs.append({"kernel": "lora_ratios", "M": M,
+                     "det8_over_atomic8": res["det8"] / res["atomic8"],
+                     "unsplit_over_det8": res["unsplit"] / res["det8"]})
+        print(f"# sweep shrink M={M}: det8 {res['det8']*1e3:.1f}us atomic {res['atomic8']*1e3:.1f}us "
+              f"unsplit {res['unsplit']*1e3:.1f}us", file=sys.stderr, flush=True)
+        del xs
+    with open(path, "w") as f:
+        for r in recs:
+            f.write(json.dumps(r) + "\n")
+
+
+def run_only(args, bi, torch, dev, X, G, H, Wq, Wkv, U, A, L, WS, La, Lu, eps):
+    """Launch one kernel ``--iters`` times (for rocprofv3 counter runs)."""
+    n = args.iters
+    if args.only == "copy":
+        # plain copy of a known size, to calibrate the HBM byte counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(n):
+            dst.copy_(src)
+    for _ in range(n):
+        if args.only == "gemm":
+            bi.bi_gemm(H, Wq, y=torch.empty((H.shape[0], Wq.shape[0]), dtype=torch.bfloat16,
+                                            device=dev))
+        elif args.only == "gemm_kv":
+            bi.bi_gemm(H, Wkv)
+        elif args.only == "rmsnorm":
+            bi.bi_rmsnorm(X, G, y=H, eps=eps)
+        elif args.only == "shrink_det8":
+            bi.bi_lora_shrink(H, A, y=L, split_k=8, ws=WS)
+        elif args.only == "shrink_atomic8":
+            bi.bi_lora_shrink_atomic(H, A, y=La, split_k=8)
+        elif args.only == "shrink_unsplit":
+            bi.bi_lora_shrink(H, A, y=Lu, split_k=1)
+    torch.cuda.synchronize()
+    print(json.dumps({"only": args.only, "iters": n}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+/*
+ * bi.h -- C ABI of libbi.so: batch-invariant reduction kernels for MI355X (gfx950).
+ *
+ * What "batch-invariant" means here.  Serving systems batch requests
+ * dynamically, so one request meets different batch partners from run to run;
+ * a kernel whose reduction order follows the batch shape then changes an
+ * unchanged request's numbers ("God Does Not Play Dice: Enforcing Batch
+ * Invariance in Agentic Kernel Generation", abstract; "Cómo superar la no
+ * determinación en la inferencia de LLM", section "La verdadera causa clave").
+ * Every entry point below except bi_lora_shrink_atomic fixes the floating-point
+ * reduction order of each output row from (N, K, R, split_k, eps) and the build
+ * alone.  An output row is therefore a pure function of its own input row and
+ * the weights: it is bitwise the same whatever the batch size M, the row's
+ * position in the batch, the other rows, the stream or the run.
+ *
+ * Conventions shared by every entry point
+ *   - bf16 values cross the ABI as raw 16-bit patterns (uint16_t); fp32 as float.
+ *   - All tensors are row-major with an explicit row stride (ld*, in elements).
+ *     Weights are stored K-contiguous: the GEMM weight W as [N, K] (one output
+ *     column per row) and the LoRA down-projection A as [R, K].
+ *   - Pointers to tensors are DEVICE pointers (hipMalloc / torch), owned by the
+ *     caller.  The library never allocates, frees or synchronises, and keeps no
+ *     mutable global state; calls are thread-safe.
+ *   - stream is a hipStream_t passed as void*; NULL means the default stream.
+ *     Every call is asynchronous on that stream.
+ *   - Return value: a bi_status.  Arguments are validated before anything is
+ *     launched; on any error nothing is launched and no output is touched.
+ *     M == 0 is valid and launches nothing.  After a launch, a HIP launch error
+ *     is reported as BI_ERR_HIP.  No exception crosses the ABI; nothing aborts.
+ *   - Alignment: every tensor base pointer must be 16-byte aligned; bf16 row
+ *     strides (and the contiguous dimension where stated) are multiples of 8
+ *     elements, fp32 row strides multiples of 4.
+ */
+#ifndef BI_H
+#define BI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BI_ABI_VERSION 1
+
+typedef enum bi_status {
+    BI_OK = 0,
+    BI_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    BI_ERR_SHAPE = 2,       /* a size or stride is out of range or not supported  */
+    BI_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned, or ld/K % 8 != 0 */
+    BI_ERR_WORKSPACE = 4,   /* split-K workspace missing or too small             */
+    BI_ERR_ALIAS = 5,       /* an output overlaps an input or another output      */
+    BI_ERR_HIP = 6,         /* the HIP runtime reported an error at launch        */
+    BI_ERR_UNSUPPORTED = 7  /* valid request this build does not implement        */
+} bi_status;
+
+/* BI_ABI_VERSION of the loaded library. */
+int bi_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *bi_status_str(int status);
+
+/*
+ * bi_rmsnorm -- y[i][k] = bf16( x[i][k] * r_i * w[k] ),
+ *               r_i = 1 / sqrt( (sum_k x[i][k]^2) / K + eps ), all in fp32.
+ *
+ * Defined by: "Cómo superar la no determinación en la inferencia de LLM",
+ * section "RMSNorm": data-parallel over the batch, each row reduced by one
+ * core, with a strategy that never changes with the batch size.  (The page's
+ * split reduction for tiny batches gives up invariance and is not offered.)
+ *
+ *   x   [M, K] bf16, row stride ldx      (input)
+ *   w   [K]    bf16                      (weight)
+ *   y   [M, K] bf16, row stride ldy      (output; may equal x when ldx == ldy)
+ *   M >= 0 rows; 8 <= K <= 16384, K % 8 == 0; eps >= 0.
+ * Reduction order of row i: one workgroup of 4 wavefronts; thread t owns the
+ * 8-element chunks t, t+256, t+512, ... and sums their squares in ascending
+ * element order; each wavefront combines its 64 lanes by a fixed xor
+ * butterfly (offsets 32, 16, 8, 4, 2, 1); the 4 wavefront sums are added as
+ * ((s0 + s1) + s2) + s3.  The tree depends on K only.  Output rounding is
+ * round-to-nearest-even.
+ */
+int bi_rmsnorm(const uint16_t *x, const uint16_t *w, uint16_t *y,
+               int64_t M, int64_t K, int64_t ldx, int64_t ldy, float eps,
+               void *stream);
+
+/*
+ * bi_gemm -- y[i][j] = bf16( sum_k x[i][k] * w[j][k] ), fp32 accumulation.
+ *
+ * Defined by: "Cómo superar la no determinación en la inferencia de LLM",
+ * section "Multiplicación de matrices (matmul)": 2-D output tiles processed
+ * data-parallel, one kernel configuration forced for every batch size, and no
+ * split of the K reduction.
+ *
+ *   x   [M, K] bf16, row stride ldx (activations)
+ *   w   [N, K] bf16, row stride ldw (weight, K-contiguous)
+ *   y   [M, N] bf16, row stride ldy (output; must not overlap x or w)
+ *   M >= 0; N >= 8, N % 8 == 0; K >= 64, K % 64 == 0.
+ * Reduction order of every output: one ascending pass over K in steps of 16
+ * (one bf16 32x32x16 matrix-core instruction per step, fp32 accumulator
+ * rounded between steps); no split-K, no stream-K.  The tile configuration is
+ * bi_gemm_config_id(N, K): it never reads M.  Output rounding is
+ * round-to-nearest-even.
+ */
+int bi_gemm(const uint16_t *x, const uint16_t *w, uint16_t *y,
+            int64_t M, int64_t N, int64_t K,
+            int64_t ldx, int64_t ldw, int64_t ldy, void *stream);
+
+/*
+ * bi_gemm_config_id -- the tile configuration bi_gemm uses for (N, K), or -1
+ * if (N, K) is not supported.  It takes no M on purpose: the configuration,
+ * and with it every output's reduction order, cannot depend on the batch size.
+ */
+int bi_gemm_config_id(int64_t N, int64_t K);
+
+/*
+ * bi_gemm_num_configs / bi_gemm_with_config -- tuning and verification hooks.
+ * bi_gemm_with_config runs bi_gemm with tile configuration `config`
+ * (0 <= config < bi_gemm_num_configs()) instead of bi_gemm_config_id(N, K).
+ * Every configuration runs the same reduction order, so all of them return the
+ * same bits; this entry point exists to demonstrate exactly that and to time
+ * the alternatives.  Same arguments and errors as bi_gemm, plus
+ * BI_ERR_UNSUPPORTED for an unknown config.
+ */
+int bi_gemm_num_configs(void);
+int bi_gemm_with_config(int config, const uint16_t *x, const uint16_t *w, uint16_t *y,
+                        int64_t M, int64_t N, int64_t K,
+                        int64_t ldx, int64_t ldw, int64_t ldy, void *stream);
+
+/*
+ * bi_lora_shrink_workspace_bytes -- bytes of workspace bi_lora_shrink needs:
+ * split_k * M * R * 4 (fp32 partials), rounded up to 256; 0 when split_k == 1.
+ */
+size_t bi_lora_shrink_workspace_bytes(int64_t M, int64_t R, int split_k);
+
+/*
+ * bi_lora_shrink -- LoRA shrink y[m][r] = sum_k x[m][k] * a[r][k], fp32 output,
+ * with a deterministic split-K.
+ *
+ * Defined by: "Reproducible LoRA Inference Through Deterministic Split-K
+ * Reduction", abstract: split-K adds parallelism to the low-rank shrink, and
+ * combining the partials in a fixed order instead of with floating-point
+ * atomics removes the run-to-run variation.
+ *
+ *   x   [M, K] bf16, row stride ldx     (activations)
+ *   a   [R, K] bf16, row stride lda     (LoRA down-projection, K-contiguous)
+ *   y   [M, R] fp32, row stride ldy     (output; ldy >= R, ldy % 4 == 0)
+ *   R == 16; split_k in {1, 2, 4, 8, 16}; K % (32 * split_k) == 0.
+ *   ws, ws_bytes: device workspace of at least
+ *       bi_lora_shrink_workspace_bytes(M, R, split_k) bytes (ignored, may be
+ *       NULL, when split_k == 1).  On return ws holds the partials
+ *       p_s[m][r] at ws[(s * M + m) * R + r] (fp32).
+ * Reduction order: chunk s covers k in [s*K/S, (s+1)*K/S); inside a chunk one
+ * ascending pass in steps of 32 (one bf16 16x16x32 matrix-core instruction per
+ * step); then y = (((p_0 + p_1) + p_2) + ...) + p_{S-1} in fp32.
+ * split_k == 1 is the unsplit reduction (one pass over all of K).
+ */
+int bi_lora_shrink(const uint16_t *x, const uint16_t *a, float *y,
+                   int64_t M, int64_t K, int64_t R,
+                   int64_t ldx, int64_t lda, int64_t ldy, int split_k,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * bi_lora_shrink_atomic -- CONTROL ONLY, NOT deterministic.  The same partial
+ * sums as bi_lora_shrink, but y is first zeroed (by a fill kernel on the same
+ * stream) and each partial is then added into y with a floating-point atomic
+ * add, in whatever order the workgroups arrive.  This is the nondeterministic
+ * combine that "Reproducible LoRA Inference Through Deterministic Split-K
+ * Reduction" (abstract) measures against; it exists to show that variation.
+ * Same arguments as bi_lora_shrink, without a workspace.
+ */
+int bi_lora_shrink_atomic(const uint16_t *x, const uint16_t *a, float *y,
+                          int64_t M, int64_t K, int64_t R,
+                          int64_t ldx, int64_t lda, int64_t ldy, int split_k,
+                          void *stream);
+
+/*
+ * bi_row_bitdiff -- bitwise comparison of rows, the invariance check.
+ *
+ * Defined by: "God Does Not Play Dice: Enforcing Batch Invariance in Agentic
+ * Kernel Generation", abstract: dynamic validation that outputs are bitwise
+ * consistent across batch contexts.
+ *
+ * For r in [0, nrows): compares row a_rows[r] of a with row b_rows[r] of b,
+ * ncols elements of elem_bytes (2 or 4) each, as raw bits, and writes
+ *   counts[2r]   = number of differing bits (popcount of the XORs)
+ *   counts[2r+1] = number of differing elements.
+ *   a, b      device pointers, row strides lda, ldb (elements)
+ *   a_rows, b_rows  device int64 row indices, or NULL for 0..nrows-1.  The
+ *                   indices are trusted: each must address a row inside its
+ *                   buffer.
+ *   counts    device uint64 [nrows][2], fully overwritten.
+ * Integer counts: exact and independent of thread order.
+ */
+int bi_row_bitdiff(const void *a, int64_t lda, const int64_t *a_rows,
+                   const void *b, int64_t ldb, const int64_t *b_rows,
+                   int64_t nrows, int64_t ncols, int elem_bytes,
+                   uint64_t *counts, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H */

@@ -1,0 +1,239 @@
+"""Thin ctypes binding of libbi.so with the C ABI's own names.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libbi.so``.  Tensors are torch CUDA (ROCm) tensors -- torch
+supplies device memory and the current stream, nothing else.  bf16 operands
+may be given as ``torch.bfloat16`` or as 16-bit integer views of the same bits.
+
+There is no fallback: importing this module raises if ``libbi.so`` has not
+been built (``python -m invariant_deterministic_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbi.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is missing: build the HIP library first "
+        "(python -m invariant_deterministic_amd.build); there is no CPU fallback")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+def _sig(name, argtypes, restype=_int):
+    f = getattr(_lib, name)
+    f.argtypes = argtypes
+    f.restype = restype
+    return f
+
+
+_lib_abi_version = _sig("bi_abi_version", [])
+_lib_status_str = _sig("bi_status_str", [_int], ctypes.c_char_p)
+_lib_rmsnorm = _sig("bi_rmsnorm", [_p, _p, _p, _i64, _i64, _i64, _i64, ctypes.c_float, _p])
+_lib_gemm = _sig("bi_gemm", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p])
+_lib_gemm_config_id = _sig("bi_gemm_config_id", [_i64, _i64])
+_lib_gemm_num_configs = _sig("bi_gemm_num_configs", [])
+_lib_gemm_with_config = _sig("bi_gemm_with_config",
+                             [_int, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p])
+_lib_ws_bytes = _sig("bi_lora_shrink_workspace_bytes", [_i64, _i64, _int], ctypes.c_size_t)
+_lib_shrink = _sig("bi_lora_shrink", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _int,
+                                      _p, ctypes.c_size_t, _p])
+_lib_shrink_atomic = _sig("bi_lora_shrink_atomic",
+                          [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _int, _p])
+_lib_row_bitdiff = _sig("bi_row_bitdiff", [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _int, _p, _p])
+
+BI_OK = 0
+EXPORTS = ("bi_abi_version", "bi_status_str", "bi_rmsnorm", "bi_gemm", "bi_gemm_config_id",
+           "bi_gemm_num_configs", "bi_gemm_with_config", "bi_lora_shrink_workspace_bytes",
+           "bi_lora_shrink", "bi_lora_shrink_atomic", "bi_row_bitdiff")
+
+
+class BiError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {bi_status_str(status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def raw() -> ctypes.CDLL:
+    """The loaded library, for ABI-level tests."""
+    return _lib
+
+
+def _check(st: int, where: str):
+    if st != BI_OK:
+        raise BiError(st, where)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+_BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _mat(t: torch.Tensor, name: str, dtypes) -> tuple[int, int]:
+    """Validate a row-major device matrix; return (data_ptr, row stride)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() == 1:
+        return t.data_ptr(), t.shape[0]
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t.data_ptr(), t.stride(0)
+
+
+def bi_abi_version() -> int:
+    return int(_lib_abi_version())
+
+
+def bi_status_str(status: int) -> str:
+    return _lib_status_str(int(status)).decode()
+
+
+def bi_rmsnorm(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,
+               eps: float = 1e-6, stream=None) -> torch.Tensor:
+    """y = RMSNorm(x) * w, one workgroup per row (see bi.h)."""
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, K), dtype=x.dtype, device=x.device)
+    px, ldx = _mat(x, "x", _BF16_LIKE)
+    pw, _ = _mat(w, "w", _BF16_LIKE)
+    py, ldy = _mat(y, "y", _BF16_LIKE)
+    if w.numel() != K or tuple(y.shape) != (M, K):
+        raise ValueError("shape mismatch")
+    _check(_lib_rmsnorm(px, pw, py, M, K, ldx, ldy, float(eps), _stream(stream)), "bi_rmsnorm")
+    return y
+
+
+def bi_gemm(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,
+            stream=None) -> torch.Tensor:
+    """y[M, N] = x[M, K] . w[N, K]^T in bf16 with fp32 accumulation (see bi.h)."""
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("x and w disagree on K")
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    px, ldx = _mat(x, "x", _BF16_LIKE)
+    pw, ldw = _mat(w, "w", _BF16_LIKE)
+    py, ldy = _mat(y, "y", _BF16_LIKE)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y has the wrong shape")
+    _check(_lib_gemm(px, pw, py, M, N, K, ldx, ldw, ldy, _stream(stream)), "bi_gemm")
+    return y
+
+
+def bi_gemm_config_id(N: int, K: int) -> int:
+    return int(_lib_gemm_config_id(N, K))
+
+
+def bi_gemm_num_configs() -> int:
+    return int(_lib_gemm_num_configs())
+
+
+def bi_gemm_with_config(config: int, x: torch.Tensor, w: torch.Tensor,
+                        y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    px, ldx = _mat(x, "x", _BF16_LIKE)
+    pw, ldw = _mat(w, "w", _BF16_LIKE)
+    py, ldy = _mat(y, "y", _BF16_LIKE)
+    _check(_lib_gemm_with_config(config, px, pw, py, M, N, K, ldx, ldw, ldy, _stream(stream)),
+           "bi_gemm_with_config")
+    return y
+
+
+def bi_lora_shrink_workspace_bytes(M: int, R: int, split_k: int) -> int:
+    return int(_lib_ws_bytes(M, R, split_k))
+
+
+def bi_lora_shrink(x: torch.Tensor, a: torch.Tensor, y: torch.Tensor | None = None,
+                   split_k: int = 8, ws: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """Deterministic split-K LoRA shrink y[M, R] = x . a^T in fp32 (see bi.h)."""
+    M, K = x.shape
+    R = a.shape[0]
+    if y is None:
+        y = torch.empty((M, R), dtype=torch.float32, device=x.device)
+    need = bi_lora_shrink_workspace_bytes(M, R, split_k)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    px, ldx = _mat(x, "x", _BF16_LIKE)
+    pa, lda = _mat(a, "a", _BF16_LIKE)
+    py, ldy = _mat(y, "y", (torch.float32,))
+    pws = ws.data_ptr() if ws is not None else None
+    nws = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_lib_shrink(px, pa, py, M, K, R, ldx, lda, ldy, split_k, pws, nws, _stream(stream)),
+           "bi_lora_shrink")
+    return y
+
+
+def bi_lora_shrink_atomic(x: torch.Tensor, a: torch.Tensor, y: torch.Tensor | None = None,
+                          split_k: int = 8, stream=None) -> torch.Tensor:
+    """CONTROL ONLY: split-K shrink combined with fp32 atomics (nondeterministic)."""
+    M, K = x.shape
+    R = a.shape[0]
+    if y is None:
+        y = torch.empty((M, R), dtype=torch.float32, device=x.device)
+    px, ldx = _mat(x, "x", _BF16_LIKE)
+    pa, lda = _mat(a, "a", _BF16_LIKE)
+    py, ldy = _mat(y, "y", (torch.float32,))
+    _check(_lib_shrink_atomic(px, pa, py, M, K, R, ldx, lda, ldy, split_k, _stream(stream)),
+           "bi_lora_shrink_atomic")
+    return y
+
+
+def bi_row_bitdiff(a: torch.Tensor, b: torch.Tensor, a_rows: torch.Tensor | None = None,
+                   b_rows: torch.Tensor | None = None, counts: torch.Tensor | None = None,
+                   stream=None, check_rows: bool = True) -> torch.Tensor:
+    """Per row pair: [differing bits, differing elements] (int64 [nrows, 2]).
+
+    ``check_rows`` verifies the index vectors on the host first (a device
+    synchronisation); pass False only for indices already known to be valid."""
+    if a.element_size() != b.element_size() or a.element_size() not in (2, 4):
+        raise TypeError("a and b need the same 2- or 4-byte element size")
+    ncols = a.shape[1]
+    if b.shape[1] != ncols:
+        raise ValueError("a and b disagree on the number of columns")
+    nrows = a_rows.numel() if a_rows is not None else (
+        b_rows.numel() if b_rows is not None else a.shape[0])
+    for rows, name in ((a_rows, "a_rows"), (b_rows, "b_rows")):
+        if rows is not None and (rows.dtype != torch.int64 or not rows.is_cuda
+                                 or rows.numel() != nrows):
+            raise ValueError(f"{name} must be a device int64 vector of {nrows} indices")
+    if check_rows and a_rows is not None and nrows and not (0 <= int(a_rows.min()) and int(a_rows.max()) < a.shape[0]):
+        raise IndexError("a_rows out of range")
+    if check_rows and b_rows is not None and nrows and not (0 <= int(b_rows.min()) and int(b_rows.max()) < b.shape[0]):
+        raise IndexError("b_rows out of range")
+    if a_rows is None and nrows > a.shape[0] or b_rows is None and nrows > b.shape[0]:
+        raise IndexError("more rows compared than present")
+    if counts is None:
+        counts = torch.empty((nrows, 2), dtype=torch.int64, device=a.device)
+    pa, lda = _mat(a, "a", (a.dtype,))
+    pb, ldb = _mat(b, "b", (b.dtype,))
+    _check(_lib_row_bitdiff(pa, lda, a_rows.data_ptr() if a_rows is not None else None,
+                            pb, ldb, b_rows.data_ptr() if b_rows is not None else None,
+                            nrows, ncols, a.element_size(), counts.data_ptr(), _stream(stream)),
+           "bi_row_bitdiff")
+    return counts

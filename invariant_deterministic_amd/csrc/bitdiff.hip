@@ -1,0 +1,78 @@
+// bitdiff.hip -- the invariance check on the device: bitwise comparison of rows.
+//
+// "God Does Not Play Dice: Enforcing Batch Invariance in Agentic Kernel
+// Generation", abstract: batch invariance is validated dynamically as bitwise
+// consistency of outputs across batch contexts.  This kernel counts, for each
+// pair of rows, the differing bits (popcount of the XOR) and the differing
+// elements.  Integer counts are exact whatever the order the threads add them.
+#include "common.h"
+
+namespace bi {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void row_bitdiff_kernel(
+    const T *__restrict__ a, int64_t lda, const int64_t *__restrict__ a_rows,
+    const T *__restrict__ b, int64_t ldb, const int64_t *__restrict__ b_rows, int64_t ncols,
+    unsigned long long *__restrict__ counts) {
+  const int64_t r = blockIdx.x;
+  const int64_t ra = a_rows ? a_rows[r] : r;
+  const int64_t rb = b_rows ? b_rows[r] : r;
+  const T *pa = a + ra * lda;
+  const T *pb = b + rb * ldb;
+  unsigned long long bits = 0, elems = 0;
+  for (int64_t c = threadIdx.x; c < ncols; c += kThreads) {
+    const uint32_t d = (uint32_t)(pa[c] ^ pb[c]);
+    bits += (unsigned long long)__popc(d);
+    elems += d ? 1ull : 0ull;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    bits += __shfl_xor(bits, off, 64);
+    elems += __shfl_xor(elems, off, 64);
+  }
+  __shared__ unsigned long long sb[kThreads / 64], se[kThreads / 64];
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sb[wv] = bits;
+    se[wv] = elems;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long tb = 0, te = 0;
+    for (int i = 0; i < kThreads / 64; ++i) {
+      tb += sb[i];
+      te += se[i];
+    }
+    counts[2 * r] = tb;
+    counts[2 * r + 1] = te;
+  }
+}
+
+}  // namespace
+}  // namespace bi
+
+using namespace bi;
+
+extern "C" int bi_row_bitdiff(const void *a, int64_t lda, const int64_t *a_rows, const void *b,
+                              int64_t ldb, const int64_t *b_rows, int64_t nrows, int64_t ncols,
+                              int elem_bytes, uint64_t *counts, void *stream) {
+  if (!a || !b || !counts) return BI_ERR_NULL;
+  if (elem_bytes != 2 && elem_bytes != 4) return BI_ERR_UNSUPPORTED;
+  if (nrows < 0 || ncols <= 0 || lda < ncols || ldb < ncols || nrows > 0x7FFFFFFF)
+    return BI_ERR_SHAPE;
+  if (((uintptr_t)a | (uintptr_t)b) & (uintptr_t)(elem_bytes - 1) || ((uintptr_t)counts & 7))
+    return BI_ERR_ALIGN;
+  if (nrows == 0) return BI_OK;
+  hipStream_t s = (hipStream_t)stream;
+  unsigned long long *c = reinterpret_cast<unsigned long long *>(counts);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(row_bitdiff_kernel<uint16_t>, dim3((unsigned)nrows), dim3(kThreads), 0, s,
+                       (const uint16_t *)a, lda, a_rows, (const uint16_t *)b, ldb, b_rows, ncols, c);
+  else
+    hipLaunchKernelGGL(row_bitdiff_kernel<uint32_t>, dim3((unsigned)nrows), dim3(kThreads), 0, s,
+                       (const uint32_t *)a, lda, a_rows, (const uint32_t *)b, ldb, b_rows, ncols, c);
+  return launch_status();
+}

@@ -1,0 +1,59 @@
+// common.h -- internal helpers shared by the HIP kernels of libbi.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bi.h"
+
+namespace bi {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16 bit pattern, round to nearest, ties to even, written with
+// integer operations so that the rounding is exactly the format's definition:
+// add half an output ulp minus one, plus the output lsb (which turns an exact
+// tie into a round-up only when the kept part is odd), then truncate.  NaN is
+// returned as a quiet NaN with its sign.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// Two bf16 in one 32-bit word (low half first) -> fp32.
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
+}
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Byte span [lo, hi) touched by a row-major [rows, cols] tensor with stride ld.
+struct Span {
+  uintptr_t lo, hi;
+};
+inline Span span_of(const void *p, int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+  uintptr_t b = (uintptr_t)p;
+  if (rows <= 0 || cols <= 0) return Span{b, b};
+  return Span{b, b + (uintptr_t)(((rows - 1) * ld + cols) * elem)};
+}
+inline bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? BI_OK : BI_ERR_HIP;
+}
+
+}  // namespace bi

@@ -1,0 +1,266 @@
+// gemm.hip -- batch-invariant bf16 GEMM for gfx950: y = bf16(x . w^T), fp32 accumulation.
+//
+// "Cómo superar la no determinación en la inferencia de LLM", section
+// "Multiplicación de matrices (matmul)": tile the output in 2-D, process tiles
+// data-parallel, and force one kernel configuration for every batch size
+// (no split-K chosen for small batches), accepting some lost speed.
+//
+// Reduction order of every output element (the batch-invariance contract):
+// one pass over k = 0, 16, 32, ..., K-16, each step a single
+// v_mfma_f32_32x32x16_bf16 whose fp32 accumulator is rounded between steps.
+// The order never depends on M, on the tile the element falls in, on the
+// position of the element inside its 32x32 matrix-core block, or on the
+// tile configuration: every configuration below runs the same instruction
+// over the same k steps; configurations differ only in how many outputs one
+// workgroup owns.  The configuration is picked from (N, K) alone.
+//
+// Data path per workgroup (4 wavefronts, 2 x 2 over the tile):
+//   HBM/L2 --global_load_lds_dwordx4--> LDS (2 stages of BK = 64)
+//          --ds_read_b128--> VGPR fragments --MFMA--> fp32 accumulators
+//   epilogue: accumulators -> bf16 (round to nearest even) -> 8-byte stores.
+// LDS rows are 128 bytes (64 bf16 of one matrix row); their eight 16-byte
+// chunks are XOR-permuted by a function of the row so that the 32 rows a
+// fragment read touches spread over all LDS banks.  Rows beyond M (or N) are
+// loaded as copies of the last valid row and never stored, so no row's
+// arithmetic depends on how many rows the batch holds.
+#include "common.h"
+
+namespace bi {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int BK = 64;                 // k per LDS stage
+constexpr int kRowBytes = BK * 2;      // one LDS row: 64 bf16
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int BN, int BM>
+struct Cfg {
+  static constexpr int WN = BN / 2, WM = BM / 2;    // wavefront tile (n x m)
+  static constexpr int FN = WN / 32, FM = WM / 32;  // 32x32 blocks per wavefront
+  static constexpr int W_BYTES = BN * kRowBytes;    // LDS bytes of the weight stage
+  static constexpr int X_BYTES = BM * kRowBytes;    // LDS bytes of the activation stage
+  static constexpr int STAGE = W_BYTES + X_BYTES;
+  static_assert(BN % 64 == 0 && BM % 64 == 0, "tile must split over 2x2 wavefronts");
+};
+
+// Map the launch index to a tile.  Workgroups are dispatched round-robin over
+// the 8 XCDs (index % 8); each XCD gets a contiguous range of logical tiles,
+// walked in groups of kGroupM tile-rows so that tiles running at the same time
+// on one XCD share weight and activation panels in that XCD's L2.  The mapping
+// changes which workgroup computes a tile, never how the tile is computed.
+constexpr int kGroupM = 4;
+__device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int &tm, int &tn) {
+  const int T = tiles_m * tiles_n;
+  const int q = T >> 3, r = T & 7;
+  const int xcd = pid & 7, local = pid >> 3;
+  const int lid = xcd * q + (xcd < r ? xcd : r) + local;
+  const int per_group = kGroupM * tiles_n;
+  const int g = lid / per_group;
+  const int first_m = g * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in_g = lid - g * per_group;
+  tm = first_m + in_g % gsize;
+  tn = in_g / gsize;
+}
+
+// Issue the direct-to-LDS loads of one BK stage of a [rows, K] operand tile.
+// Wavefront wv, instruction i fills LDS rows [i*32 + wv*8, +8): lane l writes
+// 16 bytes at row (l >> 3), physical chunk (l & 7), which holds logical chunk
+// (l & 7) ^ swz(row) of that row.
+template <int ROWS>
+__device__ __forceinline__ void load_stage(char *lds, const uint16_t *__restrict__ g, int row0,
+                                           int row_limit, int64_t ld, int k0, int wv, int lane) {
+#pragma unroll
+  for (int i = 0; i < ROWS / 32; ++i) {
+    const int r = i * 32 + wv * 8 + (lane >> 3);
+    int gr = row0 + r;
+    gr = gr < row_limit ? gr : row_limit - 1;
+    const int lc = (lane & 7) ^ swz(r);
+    const uint16_t *src = g + (int64_t)gr * ld + k0 + lc * 8;
+    lds_void *dst = (lds_void *)(lds + (i * 32 + wv * 8) * kRowBytes);
+    __builtin_amdgcn_global_load_lds((const void *)src, dst, 16, 0, 0);
+  }
+}
+
+// Fragment of 32 rows x 16 k for the 32x32x16 instruction: lane l takes row
+// (l & 31) and k = ks*16 + (l >> 5)*8 .. +7 -- the same k mapping for both
+// operands, so the instruction pairs matching k.
+__device__ __forceinline__ bf16x8 read_frag(const char *lds, int row, int ks, int lane) {
+  const int lc = ks * 2 + (lane >> 5);
+  const int off = row * kRowBytes + ((lc ^ swz(row)) << 4);
+  return *reinterpret_cast<const bf16x8 *>(lds + off);
+}
+
+template <int BN, int BM>
+struct Frags {
+  bf16x8 a[BN / 64], b[BM / 64];
+};
+
+template <int BN, int BM>
+__device__ __forceinline__ void read_frags(Frags<BN, BM> &f, const char *lds, int ks, int wn, int wm,
+                                           int lane) {
+  using C = Cfg<BN, BM>;
+#pragma unroll
+  for (int i = 0; i < C::FN; ++i) f.a[i] = read_frag(lds, wn * C::WN + i * 32 + (lane & 31), ks, lane);
+#pragma unroll
+  for (int j = 0; j < C::FM; ++j)
+    f.b[j] = read_frag(lds + C::W_BYTES, wm * C::WM + j * 32 + (lane & 31), ks, lane);
+}
+
+template <int BN, int BM>
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[BN / 64][BM / 64], const Frags<BN, BM> &f) {
+#pragma unroll
+  for (int i = 0; i < BN / 64; ++i)
+#pragma unroll
+    for (int j = 0; j < BM / 64; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+template <int BN, int BM>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+  using C = Cfg<BN, BM>;
+  __shared__ __attribute__((aligned(1024))) char lds0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds1[C::STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wv >> 1, wm = wv & 1;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int n0 = tn * BN, m0 = tm * BM;
+
+  f32x16 acc[C::FN][C::FM];
+#pragma unroll
+  for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
+
+  const int nkb = K / BK;
+  char *cur = lds0;
+  char *nxt = lds1;
+  load_stage<BN>(cur, w, n0, N, ldw, 0, wv, lane);
+  load_stage<BM>(cur + C::W_BYTES, x, m0, M, ldx, 0, wv, lane);
+  for (int kb = 0; kb < nkb; ++kb) {
+    // Stage kb has landed in `cur` for every wavefront; `nxt` is free (its
+    // last readers finished before this barrier).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kb + 1 < nkb) {
+      load_stage<BN>(nxt, w, n0, N, ldw, (kb + 1) * BK, wv, lane);
+      load_stage<BM>(nxt + C::W_BYTES, x, m0, M, ldx, (kb + 1) * BK, wv, lane);
+    }
+    Frags<BN, BM> f0, f1;
+    read_frags<BN, BM>(f0, cur, 0, wn, wm, lane);
+    read_frags<BN, BM>(f1, cur, 1, wn, wm, lane);
+    mfma_step<BN, BM>(acc, f0);
+    read_frags<BN, BM>(f0, cur, 2, wn, wm, lane);
+    mfma_step<BN, BM>(acc, f1);
+    read_frags<BN, BM>(f1, cur, 3, wn, wm, lane);
+    mfma_step<BN, BM>(acc, f0);
+    mfma_step<BN, BM>(acc, f1);
+    char *t = cur;
+    cur = nxt;
+    nxt = t;
+  }
+
+  // Epilogue.  Accumulator block (i, j) of this wavefront, register v, holds
+  // n = base_n + 8*(v/4) + 4*(lane/32) + v%4 and m = base_m + lane%32: four
+  // consecutive n of one output row per group of 4 registers -> one 8-byte store.
+#pragma unroll
+  for (int j = 0; j < C::FM; ++j) {
+    const int m = m0 + wm * C::WM + j * 32 + (lane & 31);
+    if (m >= M) continue;
+    uint16_t *yrow = y + (int64_t)m * ldy;
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * C::WN + i * 32 + q * 8 + (lane >> 5) * 4;
+        if (n < N) {
+          uint2 o;
+          o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+          o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+          *reinterpret_cast<uint2 *>(yrow + n) = o;
+        }
+      }
+    }
+  }
+}
+
+struct CfgEntry {
+  int bn, bm;
+  void (*kernel)(const uint16_t *, const uint16_t *, uint16_t *, int, int, int, int64_t,
+                 int64_t, int64_t, int, int);
+};
+
+const CfgEntry kConfigs[] = {
+    {256, 256, gemm_kernel<256, 256>},
+    {256, 128, gemm_kernel<256, 128>},
+    {128, 128, gemm_kernel<128, 128>},
+    {128, 256, gemm_kernel<128, 256>},
+};
+constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+
+int config_for(int64_t N, int64_t K) {
+  (void)K;
+  return N >= 4096 ? 0 : 2;
+}
+
+int validate(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t N, int64_t K,
+             int64_t ldx, int64_t ldw, int64_t ldy) {
+  if (!x || !w || !y) return BI_ERR_NULL;
+  if (M < 0 || N < 8 || K < BK || ldx < K || ldw < K || ldy < N || M > (1 << 30) ||
+      N > (1 << 30) || K > (1 << 30))
+    return BI_ERR_SHAPE;
+  if (K % BK) return BI_ERR_SHAPE;
+  if ((N | ldx | ldw | ldy) & 7 || !aligned16(x) || !aligned16(w) || !aligned16(y))
+    return BI_ERR_ALIGN;
+  const Span sy = span_of(y, M, N, ldy, 2);
+  if (overlap(sy, span_of(x, M, K, ldx, 2)) || overlap(sy, span_of(w, N, K, ldw, 2)))
+    return BI_ERR_ALIAS;
+  return BI_OK;
+}
+
+int launch(int cfg, const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t N,
+           int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, void *stream) {
+  const CfgEntry &c = kConfigs[cfg];
+  const int64_t tiles_m = (M + c.bm - 1) / c.bm, tiles_n = (N + c.bn - 1) / c.bn;
+  if (tiles_m * tiles_n > 0x7FFFFFFF) return BI_ERR_SHAPE;
+  hipLaunchKernelGGL(c.kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0,
+                     (hipStream_t)stream, x, w, y, (int)M, (int)N, (int)K, ldx, ldw, ldy,
+                     (int)tiles_m, (int)tiles_n);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace bi
+
+using namespace bi;
+
+extern "C" int bi_gemm_config_id(int64_t N, int64_t K) {
+  if (N < 8 || (N & 7) || K < BK || K % BK) return -1;
+  return config_for(N, K);
+}
+
+extern "C" int bi_gemm(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t N,
+                       int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, void *stream) {
+  const int st = validate(x, w, y, M, N, K, ldx, ldw, ldy);
+  if (st != BI_OK || M == 0) return st;
+  return launch(config_for(N, K), x, w, y, M, N, K, ldx, ldw, ldy, stream);
+}
+
+extern "C" int bi_gemm_num_configs(void) { return kNumConfigs; }
+
+extern "C" int bi_gemm_with_config(int config, const uint16_t *x, const uint16_t *w, uint16_t *y,
+                                   int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw,
+                                   int64_t ldy, void *stream) {
+  if (config < 0 || config >= kNumConfigs) return BI_ERR_UNSUPPORTED;
+  const int st = validate(x, w, y, M, N, K, ldx, ldw, ldy);
+  if (st != BI_OK || M == 0) return st;
+  return launch(config, x, w, y, M, N, K, ldx, ldw, ldy, stream);
+}

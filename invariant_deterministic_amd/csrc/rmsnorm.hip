@@ -1,0 +1,107 @@
+// rmsnorm.hip -- batch-invariant RMSNorm: one workgroup per row, fixed tree.
+//
+// "Cómo superar la no determinación en la inferencia de LLM", section
+// "RMSNorm": the batch-invariant form is data-parallel, each batch row reduced
+// by one core with the same strategy at every batch size.  Here one workgroup
+// (4 wavefronts of 64 lanes) owns one row; the order of its sum of squares
+// depends on K alone.  The page's split reduction for very small batches is
+// deliberately absent: it is the very change of strategy with batch size that
+// breaks invariance.
+//
+// Memory: the row is read once into registers (K <= 16384 means at most 8
+// 16-byte chunks per thread), reduced, scaled and written once: 4*K + (weight)
+// bytes per row of HBM traffic, which bounds the kernel at large M.
+#include "common.h"
+
+namespace bi {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxChunks = 8;  // 16-byte chunks per thread: K <= 8 * 256 * 8
+
+__global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
+    const uint16_t *x, const uint16_t *__restrict__ w, uint16_t *y, int K,
+    int64_t ldx, int64_t ldy, float eps) {
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int nchunks = K >> 3;
+  const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + (int64_t)row * ldx);
+
+  u32x4 v[kMaxChunks];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = t + i * kThreads;
+    if (c < nchunks) v[i] = __builtin_nontemporal_load(xr + c);
+  }
+
+  // Thread-local sum of squares in ascending element order.  Each square of a
+  // bf16 value is exact in fp32, so only the additions round.
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = t + i * kThreads;
+    if (c < nchunks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = lo_bf16(v[i][j]);
+        const float b = hi_bf16(v[i][j]);
+        ss = ss + a * a;
+        ss = ss + b * b;
+      }
+    }
+  }
+
+  // Wavefront: fixed xor butterfly.  Partners add the same two values (in
+  // swapped operand order, which is exact-commutative), so every lane ends
+  // with the same bits.
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss = ss + __shfl_xor(ss, off, 64);
+
+  __shared__ float part[kThreads / 64];
+  if ((t & 63) == 0) part[t >> 6] = ss;
+  __syncthreads();
+  const float total = ((part[0] + part[1]) + part[2]) + part[3];
+  const float r = 1.0f / sqrtf(total / (float)K + eps);
+
+  const u32x4 *wr = reinterpret_cast<const u32x4 *>(w);
+  u32x4 *yr = reinterpret_cast<u32x4 *>(y + (int64_t)row * ldy);
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = t + i * kThreads;
+    if (c < nchunks) {
+      const u32x4 wv = wr[c];
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = (lo_bf16(v[i][j]) * r) * lo_bf16(wv[j]);
+        const float hi = (hi_bf16(v[i][j]) * r) * hi_bf16(wv[j]);
+        o[j] = pack_bf16x2(lo, hi);
+      }
+      __builtin_nontemporal_store(o, yr + c);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace bi
+
+using namespace bi;
+
+extern "C" int bi_rmsnorm(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                          int64_t M, int64_t K, int64_t ldx, int64_t ldy,
+                          float eps, void *stream) {
+  if (!x || !w || !y) return BI_ERR_NULL;
+  if (M < 0 || K < 8 || K > 8 * kThreads * kMaxChunks || ldx < K || ldy < K ||
+      M > 0x7FFFFFFF || !(eps >= 0.0f))
+    return BI_ERR_SHAPE;
+  if ((K | ldx | ldy) & 7 || !aligned16(x) || !aligned16(w) || !aligned16(y))
+    return BI_ERR_ALIGN;
+  const Span sx = span_of(x, M, K, ldx, 2), sy = span_of(y, M, K, ldy, 2),
+             sw = span_of(w, 1, K, K, 2);
+  const bool in_place = (x == y) && (ldx == ldy);
+  if ((!in_place && overlap(sx, sy)) || overlap(sw, sy)) return BI_ERR_ALIAS;
+  if (M == 0) return BI_OK;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)M), dim3(kThreads), 0,
+                     (hipStream_t)stream, x, w, y, (int)K, ldx, ldy, eps);
+  return launch_status();
+}

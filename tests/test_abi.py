@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before launching anything.
+
+Every call here fails validation (or has M == 0), so no kernel is launched and
+no pointer is dereferenced: the fake device addresses are never touched.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bi.h")
+LIB = os.path.join(ROOT, "invariant_deterministic_amd", "libbi.so")
+
+BI_OK, BI_ERR_NULL, BI_ERR_SHAPE, BI_ERR_ALIGN, BI_ERR_WORKSPACE, BI_ERR_ALIAS, BI_ERR_HIP, \
+    BI_ERR_UNSUPPORTED = range(8)
+
+# fake, never-dereferenced, 16-byte aligned "device" addresses far apart
+X, W, Y, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bi_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libbi.so not built")
+    L = ctypes.CDLL(LIB)
+    p, i64, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.bi_rmsnorm.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_float, p]
+    L.bi_gemm.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, p]
+    L.bi_gemm_with_config.argtypes = [i, p, p, p, i64, i64, i64, i64, i64, i64, p]
+    L.bi_gemm_config_id.argtypes = [i64, i64]
+    L.bi_lora_shrink.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i, p, ctypes.c_size_t, p]
+    L.bi_lora_shrink_atomic.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i, p]
+    L.bi_lora_shrink_workspace_bytes.argtypes = [i64, i64, i]
+    L.bi_lora_shrink_workspace_bytes.restype = ctypes.c_size_t
+    L.bi_row_bitdiff.argtypes = [p, i64, p, p, i64, p, i64, i64, i, p, p]
+    L.bi_status_str.restype = ctypes.c_char_p
+    return L
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("bi_rmsnorm", "bi_gemm", "bi_gemm_config_id", "bi_lora_shrink",
+              "bi_lora_shrink_workspace_bytes", "bi_lora_shrink_atomic", "bi_row_bitdiff",
+              "bi_status_str", "bi_abi_version"):
+        assert n in names
+
+
+def test_every_declared_function_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in bi.h but not exported"
+
+
+def test_binding_exports_match_header():
+    import invariant_deterministic_amd.binding as b
+    assert sorted(b.EXPORTS) == declared_functions()
+    for n in b.EXPORTS:
+        assert callable(getattr(b, n))
+
+
+def test_version_and_status_strings(lib):
+    assert lib.bi_abi_version() == 1
+    for s in range(8):
+        assert lib.bi_status_str(s).decode().startswith("BI_")
+    assert lib.bi_status_str(99) == b"unknown bi_status"
+
+
+def test_rmsnorm_validation(lib):
+    f = lib.bi_rmsnorm
+    assert f(None, W, Y, 4, 4096, 4096, 4096, 1e-6, None) == BI_ERR_NULL
+    assert f(X, W, Y, -1, 4096, 4096, 4096, 1e-6, None) == BI_ERR_SHAPE
+    assert f(X, W, Y, 4, 4, 8, 8, 1e-6, None) == BI_ERR_SHAPE          # K < 8
+    assert f(X, W, Y, 4, 16392, 16392, 16392, 1e-6, None) == BI_ERR_SHAPE  # K too big
+    assert f(X, W, Y, 4, 4096, 4000, 4096, 1e-6, None) == BI_ERR_SHAPE  # ldx < K
+    assert f(X, W, Y, 4, 4096, 4096, 4096, -1.0, None) == BI_ERR_SHAPE
+    assert f(X, W, Y, 4, 4100, 4100, 4100, 1e-6, None) == BI_ERR_ALIGN  # K % 8
+    assert f(X + 8, W, Y, 4, 4096, 4096, 4096, 1e-6, None) == BI_ERR_ALIGN
+    assert f(X, W, X + 2 * 4096, 4, 4096, 4096, 4096, 1e-6, None) == BI_ERR_ALIAS
+    assert f(X, Y, Y, 4, 4096, 4096, 4096, 1e-6, None) == BI_ERR_ALIAS   # w overlaps y
+    assert f(X, W, Y, 0, 4096, 4096, 4096, 1e-6, None) == BI_OK          # M == 0: no launch
+    assert f(X, W, X, 0, 4096, 4096, 4096, 1e-6, None) == BI_OK          # in place
+
+
+def test_gemm_validation(lib):
+    f = lib.bi_gemm
+    assert f(X, None, Y, 4, 4096, 4096, 4096, 4096, 4096, None) == BI_ERR_NULL
+    assert f(X, W, Y, 4, 4096, 4000, 4000, 4000, 4096, None) == BI_ERR_SHAPE   # K % 64
+    assert f(X, W, Y, 4, 4, 4096, 4096, 4096, 4, None) == BI_ERR_SHAPE         # N < 8
+    assert f(X, W, Y, 4, 4096, 4096, 4096, 4096, 4095, None) == BI_ERR_SHAPE   # ldy < N
+    assert f(X, W, Y, 4, 4100, 4096, 4096, 4096, 4100, None) == BI_ERR_ALIGN   # N % 8
+    assert f(X, W, Y + 2, 4, 4096, 4096, 4096, 4096, 4096, None) == BI_ERR_ALIGN
+    assert f(X, W, X, 4, 4096, 4096, 4096, 4096, 4096, None) == BI_ERR_ALIAS
+    assert f(X, W, W + 64, 4, 4096, 4096, 4096, 4096, 4096, None) == BI_ERR_ALIAS
+    assert f(X, W, Y, 0, 4096, 4096, 4096, 4096, 4096, None) == BI_OK
+    assert lib.bi_gemm_with_config(99, X, W, Y, 0, 4096, 4096, 4096, 4096, 4096, None) == \
+        BI_ERR_UNSUPPORTED
+    assert lib.bi_gemm_with_config(0, X, W, Y, 0, 4096, 4096, 4096, 4096, 4096, None) == BI_OK
+
+
+def test_gemm_config_has_no_m_and_is_stable(lib):
+    for N, K in ((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336), (28672, 8192),
+                 (1024, 1024)):
+        c = lib.bi_gemm_config_id(N, K)
+        assert 0 <= c < lib.bi_gemm_num_configs()
+    assert lib.bi_gemm_config_id(4096, 100) == -1
+    assert lib.bi_gemm_config_id(4100, 4096) == -1
+
+
+def test_shrink_validation(lib):
+    f = lib.bi_lora_shrink
+    need = lib.bi_lora_shrink_workspace_bytes(4096, 16, 8)
+    assert need == 8 * 4096 * 16 * 4
+    assert lib.bi_lora_shrink_workspace_bytes(4096, 16, 1) == 0
+    assert lib.bi_lora_shrink_workspace_bytes(3, 16, 8) == 1536   # 8*3*16*4 rounded to 256
+    args = (4096, 4096, 16, 4096, 4096, 16)
+    assert f(X, W, Y, *args, 8, None, need, None) == BI_ERR_NULL
+    assert f(X, W, Y, *args, 8, WS, need - 1, None) == BI_ERR_WORKSPACE
+    assert f(X, W, Y, 4096, 4096, 8, 4096, 4096, 16, 8, WS, need, None) == BI_ERR_UNSUPPORTED
+    assert f(X, W, Y, *args, 3, WS, need, None) == BI_ERR_UNSUPPORTED
+    assert f(X, W, Y, 4096, 4000, 16, 4096, 4096, 16, 8, WS, need, None) == BI_ERR_SHAPE
+    assert f(X, W, Y, 4096, 4096, 16, 4096, 4096, 15, 8, WS, need, None) == BI_ERR_SHAPE
+    assert f(X, W, Y + 4, *args, 8, WS, need, None) == BI_ERR_ALIGN
+    assert f(X, W, Y, *args, 8, Y + 64, need, None) == BI_ERR_ALIAS
+    assert f(X, W, X, *args, 8, WS, need, None) == BI_ERR_ALIAS
+    assert f(X, W, Y, 0, 4096, 16, 4096, 4096, 16, 8, WS, 0, None) == BI_OK
+    assert f(X, W, Y, 0, 4096, 16, 4096, 4096, 16, 1, None, 0, None) == BI_OK
+    g = lib.bi_lora_shrink_atomic
+    assert g(X, None, Y, *args, 8, None) == BI_ERR_NULL
+    assert g(X, W, Y, *args, 5, None) == BI_ERR_UNSUPPORTED
+    assert g(X, W, Y, 0, 4096, 16, 4096, 4096, 16, 8, None) == BI_OK
+
+
+def test_bitdiff_validation(lib):
+    f = lib.bi_row_bitdiff
+    assert f(None, 8, None, Y, 8, None, 1, 8, 2, WS, None) == BI_ERR_NULL
+    assert f(X, 8, None, Y, 8, None, 1, 8, 3, WS, None) == BI_ERR_UNSUPPORTED
+    assert f(X, 4, None, Y, 8, None, 1, 8, 2, WS, None) == BI_ERR_SHAPE
+    assert f(X + 1, 8, None, Y, 8, None, 1, 8, 2, WS, None) == BI_ERR_ALIGN
+    assert f(X, 8, None, Y, 8, None, 0, 8, 2, WS, None) == BI_OK

@@ -1,0 +1,174 @@
+"""GPU parity, pins and batch invariance of bi_gemm against the fp64 oracle."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from invariant_deterministic_amd import synth, workloads
+from tests.gpu_util import check_bf16, dev_bf16, host_u16, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def bi():
+    need_gpu()
+    from invariant_deterministic_amd import binding
+    return binding
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, "fixed_order_pins.txt")) as f:
+        for ln in f:
+            if ln.startswith(name + " |"):
+                return [c.strip() for c in ln.split("|")]
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1024, 1024), (33, 1032, 1024), (257, 520, 4096),
+                                   (300, 4096, 640), (70, 264, 14336)])
+def test_gemm_integer_inputs_bitwise_all_configs(bi, M, N, K):
+    """Integer inputs: every fp32 partial sum is exact in any order, so each
+    configuration must equal the oracle's exact result rounded to bf16, bit for
+    bit (this pins indexing, layout, masking and the RNE epilogue)."""
+    x = synth.int_bf16((M, K), M + N, -4, 4)
+    w = synth.int_bf16((N, K), M * N, -4, 4)
+    want = oracle.bf16_round(oracle.gemm(x, w))
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    for cfg in range(bi.bi_gemm_num_configs()):
+        say(f"gemm int M={M} N={N} K={K} cfg={cfg}")
+        y = host_u16(bi.bi_gemm_with_config(cfg, X, Wt))
+        assert np.array_equal(y, want), f"cfg {cfg}: {int((y != want).sum())} mismatches"
+    assert np.array_equal(host_u16(bi.bi_gemm(X, Wt)), want)
+
+
+def test_gemm_rne_ties_in_epilogue(bi):
+    """Exact integer results 257..296 (bf16 quantum 2 there): the odd ones are
+    exact ties and must go to the even neighbour."""
+    K, N, M = 1024, 64, 40
+    x = np.zeros((M, K), np.float32)
+    x[:, 0] = 200.0
+    x[:, 1] = 57.0 + np.arange(M)
+    w = np.zeros((N, K), np.float32)
+    w[:, 0] = 1.0
+    w[:, 1] = 1.0
+    xb, wb = synth.f32_to_bf16_bits(x), synth.f32_to_bf16_bits(w)
+    y = host_u16(bi.bi_gemm(dev_bf16(xb), dev_bf16(wb)))
+    want = oracle.bf16_round(oracle.gemm(xb, wb))
+    assert np.array_equal(oracle.gemm(xb, wb)[:, 0], 257.0 + np.arange(M))
+    assert np.array_equal(y, want)
+
+
+def test_gemm_k_order_pin(bi):
+    """One ascending K pass with fp32 rounding between matrix-core steps gives
+    0x3F80; a reversed or split reduction would give 0x3F81."""
+    row = _golden("gemm_korder_ascending")
+    K = int(row[1])
+    x = np.zeros((5, K), np.float32)
+    w = np.zeros((16, K), np.float32)
+    for term in row[2].split(","):
+        k, xv_w = term.split(":")
+        xv, wv = xv_w.split("*")
+        x[:, int(k)] = float(xv)
+        w[3, int(k)] = float(wv)
+    xb, wb = synth.f32_to_bf16_bits(x), synth.f32_to_bf16_bits(w)
+    X, Wt = dev_bf16(xb), dev_bf16(wb)
+    for cfg in range(bi.bi_gemm_num_configs()):
+        y = host_u16(bi.bi_gemm_with_config(cfg, X, Wt))
+        assert np.all(y[:, 3] == int(row[4], 16)), [hex(v) for v in y[:, 3]]
+    # the exact value lies within tolerance of the pinned bits too
+    check_bf16(host_u16(bi.bi_gemm(X, Wt)), oracle.gemm(xb, wb), "k-order")
+
+
+def test_gemm_identity_and_one_hot(bi):
+    K = 1024
+    x = synth.normal_bf16((70, K), 91)
+    eye = np.zeros((K, K), np.uint16)
+    eye[np.arange(K), np.arange(K)] = 0x3F80
+    y = host_u16(bi.bi_gemm(dev_bf16(x), dev_bf16(eye)))
+    assert np.array_equal(y, x)
+    w = synth.normal_bf16((520, K), 92)
+    ks = np.array([0, 1, 15, 16, 63, 64, 511, 1023])
+    oh = np.zeros((len(ks), K), np.uint16)
+    oh[np.arange(len(ks)), ks] = 0x3F80
+    y = host_u16(bi.bi_gemm(dev_bf16(oh), dev_bf16(w)))
+    assert np.array_equal(y, w[:, ks].T)
+
+
+def test_gemm_tiny_config_parity_and_invariance(bi):
+    x, w, _ = workloads.tiny_inputs()
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    solo = np.stack([host_u16(bi.bi_gemm(X[i:i + 1], Wt))[0] for i in range(64)])
+    for M in workloads.TINY["Ms"]:
+        say(f"gemm tiny M={M}")
+        y = host_u16(bi.bi_gemm(X[:M], Wt))
+        check_bf16(y, oracle.gemm(x[:M], w), f"tiny M={M}")
+        assert np.array_equal(y, solo[:M])
+
+
+@pytest.mark.parametrize("shape_index", [0, 1, 2, 3])
+def test_gemm_llama8b_parity_sampled(bi, shape_index):
+    """Full sizes, sampled rows: the oracle computes 24 rows (including tile
+    edges) of each batch."""
+    c = workloads.LLAMA8B
+    K, N = c["shapes"][shape_index]
+    x = workloads.llama8b_x(K)
+    w = workloads.llama8b_w(shape_index)
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    for M in (1, 127, 1000, 4096, 8192):
+        say(f"gemm llama8b K={K} N={N} M={M}")
+        y = bi.bi_gemm(X[:M], Wt)
+        g = synth.rng(M)
+        rows = np.unique(np.concatenate([np.array([0, M - 1], np.int64),
+                                         np.array([r for r in (127, 128, 255, 256) if r < M], np.int64),
+                                         g.integers(0, M, size=18)])).astype(np.int64)
+        ys = host_u16(y[torch.from_numpy(rows).cuda()])
+        check_bf16(ys, oracle.gemm(x[rows], w), f"K={K} N={N} M={M}")
+
+
+def test_gemm_configs_agree_bitwise(bi):
+    """All tile configurations run the same reduction order: identical bits."""
+    x = synth.normal_bf16((300, 4096), 93)
+    w = synth.normal_bf16((1024, 4096), 94, std=0.02)
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    ref = host_u16(bi.bi_gemm_with_config(0, X, Wt))
+    for cfg in range(1, bi.bi_gemm_num_configs()):
+        assert np.array_equal(host_u16(bi.bi_gemm_with_config(cfg, X, Wt)), ref), cfg
+
+
+def test_gemm_batch_invariance_sweep(bi):
+    """Probe rows alone vs inside prefix and permuted batches over the M sweep,
+    for every Llama-3-8B shape; plus reruns."""
+    from invariant_deterministic_amd import harness
+    c = workloads.LLAMA8B
+    Ms = sorted(set(c["Ms"]) | set(c["extra_Ms"]))
+    for si, (K, N) in enumerate(c["shapes"]):
+        x = workloads.llama8b_x(K)
+        X = dev_bf16(x)
+        Wt = dev_bf16(workloads.llama8b_w(si))
+        run = lambda xb: bi.bi_gemm(xb, Wt)
+        perm = torch.from_numpy(synth.permutation(x.shape[0], c["perm_seed"]))
+        probes = [0, 1, 4, 31, 32, 126, 127, 255, 256, 999, 2038, 4092, 4095, 8190, 8191]
+        batches = harness.prefix_and_permuted_batches(Ms, x.shape[0], perm, "cuda")
+        say(f"gemm invariance K={K} N={N}: {len(batches)} batches")
+        r = harness.batch_invariance(run, X, probes, batches)
+        assert r["rows"] > 50 and r["diff_bits"] == 0, r
+        r = harness.rerun_determinism(run, X[:1000], 3)
+        assert r["diff_bits"] == 0, r
+
+
+def test_gemm_strided_and_m_zero(bi):
+    x = synth.normal_bf16((40, 1024 + 64), 95)
+    w = synth.normal_bf16((256, 1024 + 128), 96)
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    out = torch.zeros((40, 256 + 8), dtype=torch.bfloat16, device="cuda")
+    bi.bi_gemm(X[:, :1024], Wt[:, :1024], y=out[:, :256])
+    o = host_u16(out)
+    check_bf16(o[:, :256], oracle.gemm(x[:, :1024], w[:, :1024]), "strided")
+    assert np.all(o[:, 256:] == 0)
+    bi.bi_gemm(X[:0, :1024], Wt[:, :1024])
