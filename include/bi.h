@@ -25,7 +25,8 @@
  *     Every call is asynchronous on that stream.
  *   - Return value: a bi_status.  Arguments are validated before anything is
  *     launched; on any error nothing is launched and no output is touched.
- *     M == 0 is valid and launches nothing.  After a launch, a HIP launch error
+ *     M == 0 is valid and launches nothing; the [M, *] tensors (x, y and the
+ *     workspace) may then be NULL, as an empty tensor's data pointer can be.  After a launch, a HIP launch error
  *     is reported as BI_ERR_HIP.  No exception crosses the ABI; nothing aborts.
  *   - Alignment: every tensor base pointer must be 16-byte aligned; bf16 row
  *     strides (and the contiguous dimension where stated) are multiples of 8

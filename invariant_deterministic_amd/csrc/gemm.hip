@@ -213,7 +213,7 @@ int config_for(int64_t N, int64_t K) {
 
 int validate(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t N, int64_t K,
              int64_t ldx, int64_t ldw, int64_t ldy) {
-  if (!x || !w || !y) return BI_ERR_NULL;
+  if (!w || (M > 0 && (!x || !y))) return BI_ERR_NULL;
   if (M < 0 || N < 8 || K < BK || ldx < K || ldw < K || ldy < N || M > (1 << 30) ||
       N > (1 << 30) || K > (1 << 30))
     return BI_ERR_SHAPE;

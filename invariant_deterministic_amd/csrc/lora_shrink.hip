@@ -125,7 +125,7 @@ bool split_ok(int S) { return S == 1 || S == 2 || S == 4 || S == 8 || S == 16; }
 
 int validate(const uint16_t *x, const uint16_t *a, float *y, int64_t M, int64_t K, int64_t R,
              int64_t ldx, int64_t lda, int64_t ldy, int S) {
-  if (!x || !a || !y) return BI_ERR_NULL;
+  if (!a || (M > 0 && (!x || !y))) return BI_ERR_NULL;
   if (R != kR) return BI_ERR_UNSUPPORTED;
   if (!split_ok(S)) return BI_ERR_UNSUPPORTED;
   if (M < 0 || K <= 0 || M > (1 << 30) || K > (1 << 30) || ldx < K || lda < K || ldy < R)
@@ -160,7 +160,7 @@ extern "C" int bi_lora_shrink(const uint16_t *x, const uint16_t *a, float *y, in
   int st = validate(x, a, y, M, K, R, ldx, lda, ldy, split_k);
   if (st != BI_OK) return st;
   if (split_k > 1) {
-    if (!ws) return BI_ERR_NULL;
+    if (!ws && M > 0) return BI_ERR_NULL;
     if (ws_bytes < bi_lora_shrink_workspace_bytes(M, R, split_k)) return BI_ERR_WORKSPACE;
     if (!aligned16(ws)) return BI_ERR_ALIGN;
     const Span sw{(uintptr_t)ws, (uintptr_t)ws + (uintptr_t)(split_k * M * R * 4)};

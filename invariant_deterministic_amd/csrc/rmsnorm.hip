@@ -90,7 +90,7 @@ using namespace bi;
 extern "C" int bi_rmsnorm(const uint16_t *x, const uint16_t *w, uint16_t *y,
                           int64_t M, int64_t K, int64_t ldx, int64_t ldy,
                           float eps, void *stream) {
-  if (!x || !w || !y) return BI_ERR_NULL;
+  if (!w || (M > 0 && (!x || !y))) return BI_ERR_NULL;
   if (M < 0 || K < 8 || K > 8 * kThreads * kMaxChunks || ldx < K || ldy < K ||
       M > 0x7FFFFFFF || !(eps >= 0.0f))
     return BI_ERR_SHAPE;

@@ -89,6 +89,8 @@ def test_rmsnorm_validation(lib):
     assert f(X, Y, Y, 4, 4096, 4096, 4096, 1e-6, None) == BI_ERR_ALIAS   # w overlaps y
     assert f(X, W, Y, 0, 4096, 4096, 4096, 1e-6, None) == BI_OK          # M == 0: no launch
     assert f(X, W, X, 0, 4096, 4096, 4096, 1e-6, None) == BI_OK          # in place
+    assert f(None, W, None, 0, 4096, 4096, 4096, 1e-6, None) == BI_OK    # empty batch
+    assert f(None, None, None, 0, 4096, 4096, 4096, 1e-6, None) == BI_ERR_NULL
 
 
 def test_gemm_validation(lib):
@@ -102,6 +104,8 @@ def test_gemm_validation(lib):
     assert f(X, W, X, 4, 4096, 4096, 4096, 4096, 4096, None) == BI_ERR_ALIAS
     assert f(X, W, W + 64, 4, 4096, 4096, 4096, 4096, 4096, None) == BI_ERR_ALIAS
     assert f(X, W, Y, 0, 4096, 4096, 4096, 4096, 4096, None) == BI_OK
+    assert f(None, W, None, 0, 4096, 4096, 4096, 4096, 4096, None) == BI_OK
+    assert f(None, None, None, 0, 4096, 4096, 4096, 4096, 4096, None) == BI_ERR_NULL
     assert lib.bi_gemm_with_config(99, X, W, Y, 0, 4096, 4096, 4096, 4096, 4096, None) == \
         BI_ERR_UNSUPPORTED
     assert lib.bi_gemm_with_config(0, X, W, Y, 0, 4096, 4096, 4096, 4096, 4096, None) == BI_OK
@@ -134,6 +138,7 @@ def test_shrink_validation(lib):
     assert f(X, W, X, *args, 8, WS, need, None) == BI_ERR_ALIAS
     assert f(X, W, Y, 0, 4096, 16, 4096, 4096, 16, 8, WS, 0, None) == BI_OK
     assert f(X, W, Y, 0, 4096, 16, 4096, 4096, 16, 1, None, 0, None) == BI_OK
+    assert f(None, W, None, 0, 4096, 16, 4096, 4096, 16, 8, None, 0, None) == BI_OK
     g = lib.bi_lora_shrink_atomic
     assert g(X, None, Y, *args, 8, None) == BI_ERR_NULL
     assert g(X, W, Y, *args, 5, None) == BI_ERR_UNSUPPORTED
