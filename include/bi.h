@@ -96,7 +96,8 @@ int bi_rmsnorm(const uint16_t *x, const uint16_t *w, uint16_t *y,
  *   x   [M, K] bf16, row stride ldx (activations)
  *   w   [N, K] bf16, row stride ldw (weight, K-contiguous)
  *   y   [M, N] bf16, row stride ldy (output; must not overlap x or w)
- *   M >= 0; N >= 8, N % 8 == 0; K >= 64, K % 64 == 0.
+ *   M >= 0; N >= 8, N % 8 == 0; K >= 32, K % 32 == 0; x and w each span
+ *   fewer than 2^31 elements ((rows - 1) * ld + K).
  * Reduction order of every output: one ascending pass over K in steps of 16
  * (one bf16 32x32x16 matrix-core instruction per step, fp32 accumulator
  * rounded between steps); no split-K, no stream-K.  The tile configuration is

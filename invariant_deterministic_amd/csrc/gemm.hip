@@ -29,10 +29,14 @@ namespace bi {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BK = 64;                 // k per LDS stage
-constexpr int kRowBytes = BK * 2;      // one LDS row: 64 bf16
+constexpr int BK = 32;                 // k per LDS stage (two 16-k matrix-core steps)
+constexpr int kRowBytes = BK * 2;      // one LDS row: 32 bf16 = four 16-byte chunks
+constexpr int kStages = 4;             // LDS ring depth: 3 stages of loads in flight
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// Chunk permutation of LDS row r (4 chunks of 16 bytes).  The 32 rows one
+// fragment read touches map, 8 or 16 lanes at a time, onto distinct 16-byte
+// bank groups of a 128- or 256-byte LDS window.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -40,11 +44,33 @@ template <int BN, int BM>
 struct Cfg {
   static constexpr int WN = BN / 2, WM = BM / 2;    // wavefront tile (n x m)
   static constexpr int FN = WN / 32, FM = WM / 32;  // 32x32 blocks per wavefront
-  static constexpr int W_BYTES = BN * kRowBytes;    // LDS bytes of the weight stage
-  static constexpr int X_BYTES = BM * kRowBytes;    // LDS bytes of the activation stage
+  static constexpr int W_BYTES = BN * kRowBytes;    // LDS bytes of a weight stage
+  static constexpr int X_BYTES = BM * kRowBytes;    // LDS bytes of an activation stage
   static constexpr int STAGE = W_BYTES + X_BYTES;
+  static constexpr int LPS = (BN + BM) / 64;        // load instructions per wavefront per stage
   static_assert(BN % 64 == 0 && BM % 64 == 0, "tile must split over 2x2 wavefronts");
+  static_assert(3 * LPS < 64, "vmcnt range");
 };
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+// Workgroup barrier without the release/acquire fence of __syncthreads(): the
+// fence would also wait for every outstanding global->LDS load, which would
+// collapse the prefetch ring.  The waits each use needs are explicit; the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Map the launch index to a tile.  Workgroups are dispatched round-robin over
 // the 8 XCDs (index % 8); each XCD gets a contiguous range of logical tiles,
@@ -66,24 +92,32 @@ __device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int &
   tn = in_g / gsize;
 }
 
-// Issue the direct-to-LDS loads of one BK stage of a [rows, K] operand tile.
-// Wavefront wv, instruction i fills LDS rows [i*32 + wv*8, +8): lane l writes
-// 16 bytes at row (l >> 3), physical chunk (l & 7), which holds logical chunk
-// (l & 7) ^ swz(row) of that row.
+// Per-lane source offsets (in elements, relative to the stage's k0) of the
+// direct-to-LDS loads of one operand tile.  Wavefront wv, instruction i fills
+// LDS rows [i*64 + wv*16, +16): lane l writes 16 bytes at row (l >> 2),
+// physical chunk (l & 3), which holds logical chunk (l & 3) ^ swz(row).
+// Rows past the matrix edge are clamped to its last row (loaded, never stored).
 template <int ROWS>
-__device__ __forceinline__ void load_stage(char *lds, const uint16_t *__restrict__ g, int row0,
-                                           int row_limit, int64_t ld, int k0, int wv, int lane) {
+struct LoadPlan {
+  static constexpr int N = ROWS / 64;
+  int off[N];
+  __device__ __forceinline__ void init(int row0, int row_limit, int64_t ld, int wv, int lane) {
 #pragma unroll
-  for (int i = 0; i < ROWS / 32; ++i) {
-    const int r = i * 32 + wv * 8 + (lane >> 3);
-    int gr = row0 + r;
-    gr = gr < row_limit ? gr : row_limit - 1;
-    const int lc = (lane & 7) ^ swz(r);
-    const uint16_t *src = g + (int64_t)gr * ld + k0 + lc * 8;
-    lds_void *dst = (lds_void *)(lds + (i * 32 + wv * 8) * kRowBytes);
-    __builtin_amdgcn_global_load_lds((const void *)src, dst, 16, 0, 0);
+    for (int i = 0; i < N; ++i) {
+      const int r = i * 64 + wv * 16 + (lane >> 2);
+      int gr = row0 + r;
+      gr = gr < row_limit ? gr : row_limit - 1;
+      off[i] = (int)(gr * ld) + (((lane & 3) ^ swz(r)) << 3);
+    }
   }
-}
+  __device__ __forceinline__ void issue(char *lds, const uint16_t *__restrict__ g, int wv) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      lds_void *dst = (lds_void *)(lds + (i * 64 + wv * 16) * kRowBytes);
+      __builtin_amdgcn_global_load_lds((const void *)(g + off[i]), dst, 16, 0, 0);
+    }
+  }
+};
 
 // Fragment of 32 rows x 16 k for the 32x32x16 instruction: lane l takes row
 // (l & 31) and k = ks*16 + (l >> 5)*8 .. +7 -- the same k mapping for both
@@ -119,13 +153,41 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[BN / 64][BM / 64], const
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
+// Scheduling hint for the second half of a steady-state stage: alternate the
+// matrix-core instructions with the stage's global->LDS loads, then with the
+// next stage's fragment reads, so the memory instructions issue while the
+// matrix core is busy instead of in a block in front of it.
+template <int NMFMA, int NDMA, int NREAD>
+__device__ __forceinline__ void interleave() {
+  constexpr int NMEM = NDMA + NREAD;
+  constexpr int PER = (NMEM + NMFMA - 1) / NMFMA;  // memory instructions per MFMA slot
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // 1 MFMA
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int t = i * PER + j;
+      if (t < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // global->LDS
+      else if (t < NMEM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+  }
+}
+
+template <int LPS>
+__device__ __forceinline__ void wait_stages_after(int n) {
+  // wait until at most n stages (issued after the one needed) are in flight
+  if (n >= 3) wait_vmcnt<3 * LPS>();
+  else if (n == 2) wait_vmcnt<2 * LPS>();
+  else if (n == 1) wait_vmcnt<LPS>();
+  else wait_vmcnt<0>();
+}
+
 template <int BN, int BM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
     int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
   using C = Cfg<BN, BM>;
-  __shared__ __attribute__((aligned(1024))) char lds0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char lds1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * C::STAGE];
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -134,6 +196,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int n0 = tn * BN, m0 = tm * BM;
 
+  LoadPlan<BN> pw;
+  LoadPlan<BM> px;
+  pw.init(n0, N, ldw, wv, lane);
+  px.init(m0, M, ldx, wv, lane);
+
   f32x16 acc[C::FN][C::FM];
 #pragma unroll
   for (int i = 0; i < C::FN; ++i)
@@ -141,31 +208,60 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
 
   const int nkb = K / BK;
-  char *cur = lds0;
-  char *nxt = lds1;
-  load_stage<BN>(cur, w, n0, N, ldw, 0, wv, lane);
-  load_stage<BM>(cur + C::W_BYTES, x, m0, M, ldx, 0, wv, lane);
-  for (int kb = 0; kb < nkb; ++kb) {
-    // Stage kb has landed in `cur` for every wavefront; `nxt` is free (its
-    // last readers finished before this barrier).
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kb + 1 < nkb) {
-      load_stage<BN>(nxt, w, n0, N, ldw, (kb + 1) * BK, wv, lane);
-      load_stage<BM>(nxt + C::W_BYTES, x, m0, M, ldx, (kb + 1) * BK, wv, lane);
+  // Prologue: stages 0 .. kStages-1 in flight.
+#pragma unroll
+  for (int s = 0; s < kStages; ++s) {
+    if (s < nkb) {
+      char *buf = lds + s * C::STAGE;
+      pw.issue(buf, w + s * BK, wv);
+      px.issue(buf + C::W_BYTES, x + s * BK, wv);
     }
-    Frags<BN, BM> f0, f1;
-    read_frags<BN, BM>(f0, cur, 0, wn, wm, lane);
+  }
+  wait_stages_after<C::LPS>(min(kStages - 1, nkb - 1));
+  barrier_no_fence();
+
+  Frags<BN, BM> f0, f1;
+  read_frags<BN, BM>(f0, lds, 0, wn, wm, lane);
+  // Steady state (no branches inside, so the compiler's wait-count tracking
+  // sees straight-line code): stage kb computes while kb+1..kb+3 are in
+  // flight; at mid-stage, once every wavefront has its last fragments of
+  // `cur`, the barrier frees `cur` for stage kb+4.
+  int kb = 0;
+  for (; kb + kStages < nkb; ++kb) {
+    char *cur = lds + (kb & (kStages - 1)) * C::STAGE;
+    char *nxt = lds + ((kb + 1) & (kStages - 1)) * C::STAGE;
     read_frags<BN, BM>(f1, cur, 1, wn, wm, lane);
     mfma_step<BN, BM>(acc, f0);
-    read_frags<BN, BM>(f0, cur, 2, wn, wm, lane);
+    interleave<C::FN * C::FM, 0, C::FN + C::FM>();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt0();
+    wait_vmcnt<2 * C::LPS>();
+    barrier_no_fence();
+    __builtin_amdgcn_sched_barrier(0);
+    pw.issue(cur, w + (kb + kStages) * BK, wv);
+    px.issue(cur + C::W_BYTES, x + (kb + kStages) * BK, wv);
+    read_frags<BN, BM>(f0, nxt, 0, wn, wm, lane);
     mfma_step<BN, BM>(acc, f1);
-    read_frags<BN, BM>(f1, cur, 3, wn, wm, lane);
+    interleave<C::FN * C::FM, C::LPS, C::FN + C::FM>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Drain: no more stages to issue.
+  for (; kb + 1 < nkb; ++kb) {
+    char *cur = lds + (kb & (kStages - 1)) * C::STAGE;
+    char *nxt = lds + ((kb + 1) & (kStages - 1)) * C::STAGE;
+    read_frags<BN, BM>(f1, cur, 1, wn, wm, lane);
+    mfma_step<BN, BM>(acc, f0);
+    wait_lgkmcnt0();
+    wait_stages_after<C::LPS>(nkb - 2 - kb);
+    barrier_no_fence();
+    read_frags<BN, BM>(f0, nxt, 0, wn, wm, lane);
+    mfma_step<BN, BM>(acc, f1);
+  }
+  {
+    const char *cur = lds + (kb & (kStages - 1)) * C::STAGE;
+    read_frags<BN, BM>(f1, cur, 1, wn, wm, lane);
     mfma_step<BN, BM>(acc, f0);
     mfma_step<BN, BM>(acc, f1);
-    char *t = cur;
-    cur = nxt;
-    nxt = t;
   }
 
   // Epilogue.  Accumulator block (i, j) of this wavefront, register v, holds
@@ -218,6 +314,9 @@ int validate(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64
       N > (1 << 30) || K > (1 << 30))
     return BI_ERR_SHAPE;
   if (K % BK) return BI_ERR_SHAPE;
+  // the loads address each operand with 32-bit element offsets
+  if ((M > 0 && (M - 1) * ldx + K >= (int64_t(1) << 31)) || (N - 1) * ldw + K >= (int64_t(1) << 31))
+    return BI_ERR_SHAPE;
   if ((N | ldx | ldw | ldy) & 7 || !aligned16(x) || !aligned16(w) || !aligned16(y))
     return BI_ERR_ALIGN;
   const Span sy = span_of(y, M, N, ldy, 2);

@@ -29,10 +29,38 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(bi_[a-z0-9_]+)\s*\(", text)))
 
 
+class _Guarded:
+    """Wraps the library so that no call made here can reach a kernel launch:
+    a call must either fail validation or have an empty batch (M == 0)."""
+
+    # position of the batch-size argument in each launching entry point
+    M_ARG = {"bi_rmsnorm": 3, "bi_gemm": 3, "bi_gemm_with_config": 4, "bi_lora_shrink": 3,
+             "bi_lora_shrink_atomic": 3, "bi_row_bitdiff": 6}
+
+    def __init__(self, lib):
+        self._lib = lib
+
+    def __getattr__(self, name):
+        f = getattr(self._lib, name)
+        if name not in self.M_ARG:
+            return f
+
+        def call(*args):
+            r = f(*args)
+            assert r != BI_ERR_HIP, f"{name}{args} reached a launch"
+            assert r != BI_OK or args[self.M_ARG[name]] == 0, f"{name}{args} would launch"
+            return r
+        return call
+
+
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
         pytest.skip("libbi.so not built")
+    return _Guarded(_load())
+
+
+def _load():
     L = ctypes.CDLL(LIB)
     p, i64, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.bi_rmsnorm.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_float, p]
@@ -96,7 +124,8 @@ def test_rmsnorm_validation(lib):
 def test_gemm_validation(lib):
     f = lib.bi_gemm
     assert f(X, None, Y, 4, 4096, 4096, 4096, 4096, 4096, None) == BI_ERR_NULL
-    assert f(X, W, Y, 4, 4096, 4000, 4000, 4000, 4096, None) == BI_ERR_SHAPE   # K % 64
+    assert f(X, W, Y, 4, 4096, 4008, 4008, 4008, 4096, None) == BI_ERR_SHAPE   # K % 32
+    assert f(X, W, Y, 1 << 20, 4096, 4096, 4096, 4096, 4096, None) == BI_ERR_SHAPE  # x > 2^31
     assert f(X, W, Y, 4, 4, 4096, 4096, 4096, 4, None) == BI_ERR_SHAPE         # N < 8
     assert f(X, W, Y, 4, 4096, 4096, 4096, 4096, 4095, None) == BI_ERR_SHAPE   # ldy < N
     assert f(X, W, Y, 4, 4100, 4096, 4096, 4096, 4100, None) == BI_ERR_ALIGN   # N % 8
@@ -117,6 +146,7 @@ def test_gemm_config_has_no_m_and_is_stable(lib):
         c = lib.bi_gemm_config_id(N, K)
         assert 0 <= c < lib.bi_gemm_num_configs()
     assert lib.bi_gemm_config_id(4096, 100) == -1
+    assert lib.bi_gemm_config_id(4096, 96) >= 0
     assert lib.bi_gemm_config_id(4100, 4096) == -1
 
 
