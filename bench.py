@@ -47,8 +47,8 @@ def parse():
     ap.add_argument("--M", type=int, default=4096)
     ap.add_argument("--sweep", default=None)
     ap.add_argument("--only", default=None,
-                    choices=["gemm", "gemm_kv", "rmsnorm", "shrink_det8", "shrink_atomic8",
-                             "shrink_unsplit", "copy"])
+                    choices=["gemm", "gemm_kv", "gemm_up", "gemm_down", "rmsnorm", "shrink_det8",
+                             "shrink_two_pass", "shrink_atomic8", "shrink_unsplit", "copy"])
     ap.add_argument("--iters", type=int, default=50, help="launches for --only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -97,7 +97,7 @@ def main():
     print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     if args.only:
-        run_only(args, bi, torch, dev, X, G, H, Wq, Wkv, U, A, L, WS, La, Lu, eps)
+        run_only(args, bi, torch, dev, X, G, H, Wq, Wkv, Wup, Wdown, U, A, L, WS, La, Lu, eps)
         return
 
     # Probe rows: each computed alone through the whole chain, for the in-step
@@ -129,7 +129,7 @@ def main():
             if timed and big:
                 e1.record()
                 ev_pairs.append((e0, e1, 2.0 * M * w.shape[0] * w.shape[1]))
-        bi.bi_lora_shrink(H, A, y=L, split_k=8, ws=WS)
+        bi.bi_lora_shrink(H, A, y=L, split_k=8)
         bi.bi_lora_shrink(H, A, y=Lu, split_k=1)
         bi.bi_lora_shrink_atomic(H, A, y=La, split_k=8)
         bi.bi_row_bitdiff(Q, solo_q, probe_pos, probe_ids, counts=counts_q, check_rows=False)
@@ -292,7 +292,8 @@ def sweep(path, bi, torch, dev, to_dev):
         ws = torch.empty(bi.bi_lora_shrink_workspace_bytes(M, 16, 8), dtype=torch.uint8, device=dev)
         by = 2.0 * M * 4096 + 2 * 16 * 4096 + 4 * M * 16
         res = {}
-        for name, fn in (("det8", lambda i: bi.bi_lora_shrink(xs[i % c], a, y=y, split_k=8, ws=ws)),
+        for name, fn in (("det8", lambda i: bi.bi_lora_shrink(xs[i % c], a, y=y, split_k=8)),
+                         ("det8_two_pass", lambda i: bi.bi_lora_shrink_two_pass(xs[i % c], a, y=y, split_k=8, ws=ws)),
                          ("unsplit", lambda i: bi.bi_lora_shrink(xs[i % c], a, y=y, split_k=1)),
                          ("atomic8", lambda i: bi.bi_lora_shrink_atomic(xs[i % c], a, y=y, split_k=8))):
             ms = _time_loop(torch, fn, 4 * c)
@@ -303,7 +304,8 @@ def sweep(path, bi, torch, dev, to_dev):
         recs.append({"kernel": "lora_ratios", "M": M,
                      "det8_over_atomic8": res["det8"] / res["atomic8"],
                      "unsplit_over_det8": res["unsplit"] / res["det8"]})
-        print(f"# sweep shrink M={M}: det8 {res['det8']*1e3:.1f}us atomic {res['atomic8']*1e3:.1f}us "
+        print(f"# sweep shrink M={M}: det8 {res['det8']*1e3:.1f}us two-pass {res['det8_two_pass']*1e3:.1f}us "
+              f"atomic {res['atomic8']*1e3:.1f}us "
               f"unsplit {res['unsplit']*1e3:.1f}us", file=sys.stderr, flush=True)
         del xs
     with open(path, "w") as f:
@@ -311,25 +313,41 @@ def sweep(path, bi, torch, dev, to_dev):
             f.write(json.dumps(r) + "\n")
 
 
-def run_only(args, bi, torch, dev, X, G, H, Wq, Wkv, U, A, L, WS, La, Lu, eps):
+def run_only(args, bi, torch, dev, X, G, H, Wq, Wkv, Wup, Wdown, U, A, L, WS, La, Lu, eps):
     """Launch one kernel ``--iters`` times (for rocprofv3 counter runs)."""
     n = args.iters
     if args.only == "copy":
-        # plain copy of a known size, to calibrate the HBM byte counters
+        # a plain device copy of known size (256 MiB), to calibrate the HBM
+        # byte counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(n):
             dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "iters": n, "bytes_each_way": 256 << 20}), flush=True)
+        return
+    bi.bi_rmsnorm(X, G, y=H, eps=eps)
+    U.copy_(torch.randn(U.shape, device=dev).to(torch.bfloat16))
+    Q = torch.empty((H.shape[0], Wq.shape[0]), dtype=torch.bfloat16, device=dev)
+    KV = torch.empty((H.shape[0], Wkv.shape[0]), dtype=torch.bfloat16, device=dev)
+    U2 = torch.empty_like(U)
+    D = torch.empty((H.shape[0], Wdown.shape[0]), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
     for _ in range(n):
         if args.only == "gemm":
-            bi.bi_gemm(H, Wq, y=torch.empty((H.shape[0], Wq.shape[0]), dtype=torch.bfloat16,
-                                            device=dev))
+            bi.bi_gemm(H, Wq, y=Q)
         elif args.only == "gemm_kv":
-            bi.bi_gemm(H, Wkv)
+            bi.bi_gemm(H, Wkv, y=KV)
+        elif args.only == "gemm_up":
+            bi.bi_gemm(H, Wup, y=U2)
+        elif args.only == "gemm_down":
+            bi.bi_gemm(U, Wdown, y=D)
         elif args.only == "rmsnorm":
             bi.bi_rmsnorm(X, G, y=H, eps=eps)
         elif args.only == "shrink_det8":
-            bi.bi_lora_shrink(H, A, y=L, split_k=8, ws=WS)
+            bi.bi_lora_shrink(H, A, y=L, split_k=8)
+        elif args.only == "shrink_two_pass":
+            bi.bi_lora_shrink_two_pass(H, A, y=L, split_k=8, ws=WS)
         elif args.only == "shrink_atomic8":
             bi.bi_lora_shrink_atomic(H, A, y=La, split_k=8)
         elif args.only == "shrink_unsplit":

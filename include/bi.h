@@ -148,10 +148,11 @@ size_t bi_lora_shrink_workspace_bytes(int64_t M, int64_t R, int split_k);
  *   a   [R, K] bf16, row stride lda     (LoRA down-projection, K-contiguous)
  *   y   [M, R] fp32, row stride ldy     (output; ldy >= R, ldy % 4 == 0)
  *   R == 16; split_k in {1, 2, 4, 8, 16}; K % (32 * split_k) == 0.
- *   ws, ws_bytes: device workspace of at least
- *       bi_lora_shrink_workspace_bytes(M, R, split_k) bytes (ignored, may be
- *       NULL, when split_k == 1).  On return ws holds the partials
- *       p_s[m][r] at ws[(s * M + m) * R + r] (fp32).
+ *   ws, ws_bytes: optional.  One kernel computes the split_k partials of each
+ *       16-row block in split_k wavefronts of one workgroup and combines them
+ *       through LDS.  If ws is not NULL (and split_k > 1) it must hold
+ *       bi_lora_shrink_workspace_bytes(M, R, split_k) bytes and receives the
+ *       partials p_s[m][r] at ws[(s * M + m) * R + r] (fp32) as well.
  * Reduction order: chunk s covers k in [s*K/S, (s+1)*K/S); inside a chunk one
  * ascending pass in steps of 32 (one bf16 16x16x32 matrix-core instruction per
  * step); then y = (((p_0 + p_1) + p_2) + ...) + p_{S-1} in fp32.
@@ -163,10 +164,22 @@ int bi_lora_shrink(const uint16_t *x, const uint16_t *a, float *y,
                    void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * bi_lora_shrink_two_pass -- the same result, bit for bit, with the split
+ * spread over workgroups: the partials go through the caller's fp32 workspace
+ * in HBM (ws, required when split_k > 1, layout as above) and a second kernel
+ * combines them in the same fixed order.  Kept to measure that design against
+ * the single-kernel one.  Same arguments and errors as bi_lora_shrink.
+ */
+int bi_lora_shrink_two_pass(const uint16_t *x, const uint16_t *a, float *y,
+                            int64_t M, int64_t K, int64_t R,
+                            int64_t ldx, int64_t lda, int64_t ldy, int split_k,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
  * bi_lora_shrink_atomic -- CONTROL ONLY, NOT deterministic.  The same partial
  * sums as bi_lora_shrink, but y is first zeroed (by a fill kernel on the same
  * stream) and each partial is then added into y with a floating-point atomic
- * add, in whatever order the workgroups arrive.  This is the nondeterministic
+ * add, in whatever order the wavefronts arrive.  This is the nondeterministic
  * combine that "Reproducible LoRA Inference Through Deterministic Split-K
  * Reduction" (abstract) measures against; it exists to show that variation.
  * Same arguments as bi_lora_shrink, without a workspace.

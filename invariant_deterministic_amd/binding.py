@@ -47,6 +47,8 @@ _lib_gemm_with_config = _sig("bi_gemm_with_config",
 _lib_ws_bytes = _sig("bi_lora_shrink_workspace_bytes", [_i64, _i64, _int], ctypes.c_size_t)
 _lib_shrink = _sig("bi_lora_shrink", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _int,
                                       _p, ctypes.c_size_t, _p])
+_lib_shrink_two_pass = _sig("bi_lora_shrink_two_pass", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64,
+                                                        _i64, _int, _p, ctypes.c_size_t, _p])
 _lib_shrink_atomic = _sig("bi_lora_shrink_atomic",
                           [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _int, _p])
 _lib_row_bitdiff = _sig("bi_row_bitdiff", [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _int, _p, _p])
@@ -54,7 +56,7 @@ _lib_row_bitdiff = _sig("bi_row_bitdiff", [_p, _i64, _p, _p, _i64, _p, _i64, _i6
 BI_OK = 0
 EXPORTS = ("bi_abi_version", "bi_status_str", "bi_rmsnorm", "bi_gemm", "bi_gemm_config_id",
            "bi_gemm_num_configs", "bi_gemm_with_config", "bi_lora_shrink_workspace_bytes",
-           "bi_lora_shrink", "bi_lora_shrink_atomic", "bi_row_bitdiff")
+           "bi_lora_shrink", "bi_lora_shrink_two_pass", "bi_lora_shrink_atomic", "bi_row_bitdiff")
 
 
 class BiError(RuntimeError):
@@ -171,21 +173,33 @@ def bi_lora_shrink_workspace_bytes(M: int, R: int, split_k: int) -> int:
 def bi_lora_shrink(x: torch.Tensor, a: torch.Tensor, y: torch.Tensor | None = None,
                    split_k: int = 8, ws: torch.Tensor | None = None,
                    stream=None) -> torch.Tensor:
-    """Deterministic split-K LoRA shrink y[M, R] = x . a^T in fp32 (see bi.h)."""
+    """Deterministic split-K LoRA shrink y[M, R] = x . a^T in fp32, one kernel
+    (see bi.h); ``ws`` is optional and, when given, receives the partials."""
+    return _shrink(_lib_shrink, "bi_lora_shrink", x, a, y, split_k, ws, stream, False)
+
+
+def bi_lora_shrink_two_pass(x: torch.Tensor, a: torch.Tensor, y: torch.Tensor | None = None,
+                            split_k: int = 8, ws: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """Same bits as bi_lora_shrink, via an HBM workspace and a second kernel."""
+    return _shrink(_lib_shrink_two_pass, "bi_lora_shrink_two_pass", x, a, y, split_k, ws, stream,
+                   True)
+
+
+def _shrink(fn, name, x, a, y, split_k, ws, stream, need_ws):
     M, K = x.shape
     R = a.shape[0]
     if y is None:
         y = torch.empty((M, R), dtype=torch.float32, device=x.device)
     need = bi_lora_shrink_workspace_bytes(M, R, split_k)
-    if ws is None and need > 0:
+    if ws is None and need > 0 and need_ws:
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     px, ldx = _mat(x, "x", _BF16_LIKE)
     pa, lda = _mat(a, "a", _BF16_LIKE)
     py, ldy = _mat(y, "y", (torch.float32,))
     pws = ws.data_ptr() if ws is not None else None
     nws = ws.numel() * ws.element_size() if ws is not None else 0
-    _check(_lib_shrink(px, pa, py, M, K, R, ldx, lda, ldy, split_k, pws, nws, _stream(stream)),
-           "bi_lora_shrink")
+    _check(fn(px, pa, py, M, K, R, ldx, lda, ldy, split_k, pws, nws, _stream(stream)), name)
     return y
 
 

@@ -7,16 +7,26 @@
 // between identical runs, while a combine in a fixed order does not, at a small
 // latency cost over the atomic version and a speed-up over no split at all.
 //
-// Reduction order (batch- and run-invariant for every mode but ATOMIC):
+// Reduction order (batch- and run-invariant for every path but the atomic one):
 //   chunk s covers k in [s*Kc, (s+1)*Kc), Kc = K / S; inside a chunk, one
 //   ascending pass in steps of 32 k, one v_mfma_f32_16x16x32_bf16 per step,
 //   fp32 accumulator rounded between steps; then
 //   y = (((p_0 + p_1) + p_2) + ...) + p_{S-1} in fp32.
-// S == 1 is the unsplit reduction: one pass over all of K, stored directly.
+// S == 1 is the unsplit reduction: one pass over all of K.
 //
-// Work split: a workgroup is 4 wavefronts x 16 rows = 64 rows of x, for one
-// chunk (grid.y = S).  The shrink reads x once from HBM (2*K bytes a row) and
-// the small a (R*K*2 bytes) from cache, so it is bound by HBM bandwidth.
+// Three ways to run it, all computing the same partials p_s:
+//   fused     (bi_lora_shrink): one kernel.  A workgroup is S wavefronts over
+//             one 16-row block; wavefront s computes p_s, the S partials meet in
+//             LDS (the on-chip fp32 workspace) and wavefront 0 folds them in
+//             order.  No second launch, no atomics, no counters.
+//   two-pass  (bi_lora_shrink_two_pass): the split spans workgroups; partials go
+//             through the caller's fp32 workspace in HBM and a second kernel
+//             folds them in order.  Same bits as fused.
+//   atomic    (bi_lora_shrink_atomic): the fused layout, but each wavefront adds
+//             its partial into the zeroed output with a floating-point atomic,
+//             in arrival order.  The nondeterministic control.
+// The shrink reads x once from HBM (2*K bytes a row) and the small a from
+// cache, so it is bound by HBM bandwidth.
 #include "common.h"
 
 namespace bi {
@@ -100,6 +110,96 @@ __global__ __launch_bounds__(kThreads) void shrink_partial_kernel(
   }
 }
 
+// Fused split-K: blockDim = 64 * S; wavefront s computes p_s of the 16 rows
+// [blockIdx.x * 16, +16) over chunk s.  Same operand roles, k mapping and step
+// order as shrink_partial_kernel.  MODE: kStoreOut folds through LDS (and, if
+// ws != nullptr, also stores each p_s there); kAtomic adds each p_s into y.
+template <int S, int MODE>
+__global__ __launch_bounds__(64 * S) void shrink_fused_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ a, float *__restrict__ y,
+    float *__restrict__ ws, int M, int K, int64_t ldx, int64_t lda, int64_t ldy) {
+  const int lane = threadIdx.x & 63;
+  const int s = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * kRowsPerWave;
+  const int chunk = K / S;
+  const int k0 = s * chunk;
+  const int steps = chunk / kStep;
+
+  int gm = m0 + (lane & 15);
+  gm = gm < M ? gm : M - 1;  // rows past M read a copy of the last row, never stored
+  const int koff = (lane >> 4) * 8;
+  const bf16x8 *xp = reinterpret_cast<const bf16x8 *>(x + (int64_t)gm * ldx + k0 + koff);
+  const bf16x8 *ap = reinterpret_cast<const bf16x8 *>(a + (int64_t)(lane & 15) * lda + k0 + koff);
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 xf[kGroup], af[kGroup];
+  const int ngroups = (steps + kGroup - 1) / kGroup;
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    if (i < steps) {
+      xf[i] = __builtin_nontemporal_load(xp + i * (kStep / 8));
+      af[i] = ap[i * (kStep / 8)];
+    }
+  }
+  for (int g = 0; g < ngroups; ++g) {
+    bf16x8 xn[kGroup], an[kGroup];
+    const int base = (g + 1) * kGroup;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      if (base + i < steps) {
+        xn[i] = __builtin_nontemporal_load(xp + (base + i) * (kStep / 8));
+        an[i] = ap[(base + i) * (kStep / 8)];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      if (g * kGroup + i < steps) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], xf[i], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      xf[i] = xn[i];
+      af[i] = an[i];
+    }
+  }
+
+  const int m = m0 + (lane & 15);
+  const int r0 = (lane >> 4) * 4;
+  if (MODE == kAtomic) {
+    if (m < M) {
+      float *o = y + (int64_t)m * ldy + r0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) unsafeAtomicAdd(o + v, acc[v]);
+    }
+    return;
+  }
+  if (S == 1) {
+    if (m < M) *reinterpret_cast<f32x4 *>(y + (int64_t)m * ldy + r0) = acc;
+    return;
+  }
+  if (ws != nullptr && m < M) *reinterpret_cast<f32x4 *>(ws + ((int64_t)s * M + m) * kR + r0) = acc;
+  __shared__ f32x4 part[S][64];
+  part[s][lane] = acc;
+  __syncthreads();
+  if (s == 0 && m < M) {
+    f32x4 t = part[0][lane];
+#pragma unroll
+    for (int q = 1; q < S; ++q) t = t + part[q][lane];  // element-wise fp32, q ascending
+    *reinterpret_cast<f32x4 *>(y + (int64_t)m * ldy + r0) = t;
+  }
+}
+
+template <int MODE>
+void launch_fused(int S, dim3 grid, hipStream_t st, const uint16_t *x, const uint16_t *a, float *y,
+                  float *ws, int M, int K, int64_t ldx, int64_t lda, int64_t ldy) {
+  switch (S) {
+    case 1: hipLaunchKernelGGL((shrink_fused_kernel<1, MODE>), grid, dim3(64), 0, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
+    case 2: hipLaunchKernelGGL((shrink_fused_kernel<2, MODE>), grid, dim3(128), 0, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
+    case 4: hipLaunchKernelGGL((shrink_fused_kernel<4, MODE>), grid, dim3(256), 0, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
+    case 8: hipLaunchKernelGGL((shrink_fused_kernel<8, MODE>), grid, dim3(512), 0, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
+    default: hipLaunchKernelGGL((shrink_fused_kernel<16, MODE>), grid, dim3(1024), 0, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
+  }
+}
+
 // Fixed-order combine: y[m][r] = (((p_0 + p_1) + p_2) + ...) + p_{S-1}.
 __global__ __launch_bounds__(kThreads) void shrink_combine_kernel(const float *__restrict__ ws,
                                                                   float *__restrict__ y, int M,
@@ -139,6 +239,17 @@ int validate(const uint16_t *x, const uint16_t *a, float *y, int64_t M, int64_t 
   return BI_OK;
 }
 
+int validate_ws(const uint16_t *x, const uint16_t *a, float *y, int64_t M, int64_t K, int64_t R,
+                int64_t ldx, int64_t lda, int64_t ldy, int S, void *ws, size_t ws_bytes) {
+  if (ws_bytes < bi_lora_shrink_workspace_bytes(M, R, S)) return BI_ERR_WORKSPACE;
+  if (!aligned16(ws)) return BI_ERR_ALIGN;
+  const Span sw{(uintptr_t)ws, (uintptr_t)ws + (uintptr_t)(S * M * R * 4)};
+  if (overlap(sw, span_of(y, M, R, ldy, 4)) || overlap(sw, span_of(x, M, K, ldx, 2)) ||
+      overlap(sw, span_of(a, R, K, lda, 2)))
+    return BI_ERR_ALIAS;
+  return BI_OK;
+}
+
 dim3 partial_grid(int64_t M, int S) {
   return dim3((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)S);
 }
@@ -159,14 +270,23 @@ extern "C" int bi_lora_shrink(const uint16_t *x, const uint16_t *a, float *y, in
                               void *ws, size_t ws_bytes, void *stream) {
   int st = validate(x, a, y, M, K, R, ldx, lda, ldy, split_k);
   if (st != BI_OK) return st;
+  if (split_k > 1 && ws != nullptr && (st = validate_ws(x, a, y, M, K, R, ldx, lda, ldy, split_k, ws, ws_bytes)) != BI_OK)
+    return st;
+  if (M == 0) return BI_OK;
+  launch_fused<kStoreOut>(split_k, dim3((unsigned)((M + kRowsPerWave - 1) / kRowsPerWave)),
+                          (hipStream_t)stream, x, a, y, split_k > 1 ? static_cast<float *>(ws) : nullptr,
+                          (int)M, (int)K, ldx, lda, ldy);
+  return launch_status();
+}
+
+extern "C" int bi_lora_shrink_two_pass(const uint16_t *x, const uint16_t *a, float *y, int64_t M,
+                                       int64_t K, int64_t R, int64_t ldx, int64_t lda, int64_t ldy,
+                                       int split_k, void *ws, size_t ws_bytes, void *stream) {
+  int st = validate(x, a, y, M, K, R, ldx, lda, ldy, split_k);
+  if (st != BI_OK) return st;
   if (split_k > 1) {
     if (!ws && M > 0) return BI_ERR_NULL;
-    if (ws_bytes < bi_lora_shrink_workspace_bytes(M, R, split_k)) return BI_ERR_WORKSPACE;
-    if (!aligned16(ws)) return BI_ERR_ALIGN;
-    const Span sw{(uintptr_t)ws, (uintptr_t)ws + (uintptr_t)(split_k * M * R * 4)};
-    if (overlap(sw, span_of(y, M, R, ldy, 4)) || overlap(sw, span_of(x, M, K, ldx, 2)) ||
-        overlap(sw, span_of(a, R, K, lda, 2)))
-      return BI_ERR_ALIAS;
+    if ((st = validate_ws(x, a, y, M, K, R, ldx, lda, ldy, split_k, ws, ws_bytes)) != BI_OK) return st;
   }
   if (M == 0) return BI_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -196,7 +316,7 @@ extern "C" int bi_lora_shrink_atomic(const uint16_t *x, const uint16_t *a, float
   hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, s, y, (int)M, ldy);
   if ((st = launch_status()) != BI_OK) return st;
-  hipLaunchKernelGGL(shrink_partial_kernel<kAtomic>, partial_grid(M, split_k), dim3(kThreads), 0,
-                     s, x, a, y, (int)M, (int)K, ldx, lda, ldy, (int)(K / split_k));
+  launch_fused<kAtomic>(split_k, dim3((unsigned)((M + kRowsPerWave - 1) / kRowsPerWave)), s, x, a, y,
+                        nullptr, (int)M, (int)K, ldx, lda, ldy);
   return launch_status();
 }

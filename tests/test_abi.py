@@ -35,7 +35,7 @@ class _Guarded:
 
     # position of the batch-size argument in each launching entry point
     M_ARG = {"bi_rmsnorm": 3, "bi_gemm": 3, "bi_gemm_with_config": 4, "bi_lora_shrink": 3,
-             "bi_lora_shrink_atomic": 3, "bi_row_bitdiff": 6}
+             "bi_lora_shrink_two_pass": 3, "bi_lora_shrink_atomic": 3, "bi_row_bitdiff": 6}
 
     def __init__(self, lib):
         self._lib = lib
@@ -68,6 +68,7 @@ def _load():
     L.bi_gemm_with_config.argtypes = [i, p, p, p, i64, i64, i64, i64, i64, i64, p]
     L.bi_gemm_config_id.argtypes = [i64, i64]
     L.bi_lora_shrink.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i, p, ctypes.c_size_t, p]
+    L.bi_lora_shrink_two_pass.argtypes = L.bi_lora_shrink.argtypes
     L.bi_lora_shrink_atomic.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i, p]
     L.bi_lora_shrink_workspace_bytes.argtypes = [i64, i64, i]
     L.bi_lora_shrink_workspace_bytes.restype = ctypes.c_size_t
@@ -157,7 +158,9 @@ def test_shrink_validation(lib):
     assert lib.bi_lora_shrink_workspace_bytes(4096, 16, 1) == 0
     assert lib.bi_lora_shrink_workspace_bytes(3, 16, 8) == 1536   # 8*3*16*4 rounded to 256
     args = (4096, 4096, 16, 4096, 4096, 16)
-    assert f(X, W, Y, *args, 8, None, need, None) == BI_ERR_NULL
+    assert lib.bi_lora_shrink_two_pass(X, W, Y, *args, 8, None, need, None) == BI_ERR_NULL
+    assert lib.bi_lora_shrink_two_pass(X, W, Y, *args, 8, WS, need - 1, None) == BI_ERR_WORKSPACE
+    assert lib.bi_lora_shrink_two_pass(X, W, Y, 0, 4096, 16, 4096, 4096, 16, 8, None, 0, None) == BI_OK
     assert f(X, W, Y, *args, 8, WS, need - 1, None) == BI_ERR_WORKSPACE
     assert f(X, W, Y, 4096, 4096, 8, 4096, 4096, 16, 8, WS, need, None) == BI_ERR_UNSUPPORTED
     assert f(X, W, Y, *args, 3, WS, need, None) == BI_ERR_UNSUPPORTED

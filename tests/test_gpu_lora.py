@@ -30,12 +30,14 @@ def _golden(name):
     raise KeyError(name)
 
 
-VARIANTS = ("det8", "unsplit", "atomic8")
+VARIANTS = ("det8", "det8_two_pass", "unsplit", "atomic8")
 
 
 def run_variant(bi, name, X, A, y=None, ws=None):
     if name == "det8":
-        return bi.bi_lora_shrink(X, A, y=y, split_k=8, ws=ws)
+        return bi.bi_lora_shrink(X, A, y=y, split_k=8)
+    if name == "det8_two_pass":
+        return bi.bi_lora_shrink_two_pass(X, A, y=y, split_k=8, ws=ws)
     if name == "unsplit":
         return bi.bi_lora_shrink(X, A, y=y, split_k=1)
     return bi.bi_lora_shrink_atomic(X, A, y=y, split_k=8)
@@ -62,6 +64,7 @@ def test_shrink_integer_inputs_bitwise(bi, split):
         X, A = dev_bf16(x), dev_bf16(a)
         say(f"shrink int split={split} M={M}")
         assert np.array_equal(host_f32(bi.bi_lora_shrink(X, A, split_k=split)), want)
+        assert np.array_equal(host_f32(bi.bi_lora_shrink_two_pass(X, A, split_k=split)), want)
         assert np.array_equal(host_f32(bi.bi_lora_shrink_atomic(X, A, split_k=split)), want)
 
 
@@ -90,15 +93,29 @@ def test_shrink_combine_order_pin(bi):
     x, a, row = _assoc_rows(M, pos)
     X, A = dev_bf16(x), dev_bf16(a)
     det = host_u32(bi.bi_lora_shrink(X, A, split_k=8))
+    two = host_u32(bi.bi_lora_shrink_two_pass(X, A, split_k=8))
     uns = host_u32(bi.bi_lora_shrink(X, A, split_k=1))
     want = int(row[4], 16)
     assert np.all(det[pos] == want), [hex(v) for v in det[pos].ravel()]
+    assert np.all(two[pos] == want)
     assert np.all(uns[pos] == int(_golden("shrink_unsplit")[4], 16))
     allowed = {int(v, 16) for v in _golden("shrink_atomic_any_of")[4].split(",")}
     for _ in range(20):
         at = host_u32(bi.bi_lora_shrink_atomic(X, A, split_k=8))
         assert set(at[pos].ravel().tolist()) <= allowed
     check_f32(host_f32(bi.bi_lora_shrink(X, A, split_k=8)), oracle.lora_shrink(x, a), "pin rows")
+
+
+@pytest.mark.parametrize("split", [1, 2, 4, 8, 16])
+def test_shrink_fused_equals_two_pass_bitwise(bi, split):
+    """The single-kernel (LDS) combine and the two-pass (HBM workspace) combine
+    compute the same partials and fold them in the same order: same bits."""
+    for M in (1, 5, 64, 1000):
+        x, a = workloads.lora_inputs(M)
+        X, A = dev_bf16(x), dev_bf16(a)
+        f = host_u32(bi.bi_lora_shrink(X, A, split_k=split))
+        t = host_u32(bi.bi_lora_shrink_two_pass(X, A, split_k=split))
+        assert np.array_equal(f, t), (split, M)
 
 
 def test_shrink_workspace_partials_and_exact_combine(bi):
@@ -110,6 +127,9 @@ def test_shrink_workspace_partials_and_exact_combine(bi):
     ws = torch.zeros(bi.bi_lora_shrink_workspace_bytes(M, 16, 8), dtype=torch.uint8, device="cuda")
     y = host_f32(bi.bi_lora_shrink(X, A, split_k=8, ws=ws))
     p = host_f32(ws.view(torch.float32)[: 8 * M * 16]).reshape(8, M, 16)
+    ws2 = torch.zeros_like(ws)
+    y2 = host_f32(bi.bi_lora_shrink_two_pass(X, A, split_k=8, ws=ws2))
+    assert np.array_equal(host_u32(ws2), host_u32(ws)) and np.array_equal(y2.view(np.uint32), y.view(np.uint32))
     ch = K // 8
     for s in range(8):
         check_f32(p[s], oracle.gemm(x[:, s * ch:(s + 1) * ch].copy(), a[:, s * ch:(s + 1) * ch].copy()),
