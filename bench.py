@@ -167,7 +167,8 @@ def main():
     achieved = avg_flop / (avg_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "kernel": "gemm_kernel<256,256> (Q, U, D projections)",
+                "traffic": recorded_traffic(), "traffic_unit": "HBM bytes per launch (rocprofv3)",
+                "kernel": "gemm_kernel<256,256> (Q, U, D projections)",
                 "avg_launch_us": round(avg_ms * 1e3, 2),
                 "flop_per_launch": avg_flop}
 
@@ -191,13 +192,37 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_kernel_256x256_llama8b_m4096_hbm.txt")
+GEMM_SOURCE = os.path.join(ROOT, "invariant_deterministic_amd", "csrc", "gemm.hip")
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dominant GEMM from the committed rocprofv3
+    counter summary, or None when the kernel source changed since."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.split()[0] if v.split() else ""
+    cur = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != cur or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(x, g, ws_h, a, eps):
-    """The oracle as it stands, on a bounded sample of one step: 16 rows through
-    RMSNorm, the four projections and the shrink (about 4.4 GFLOP of fp64)."""
+    """The oracle as it stands, on a bounded sample of one step: 64 rows through
+    RMSNorm, the four projections and the shrink (about 25 GFLOP of fp64,
+    10-20 s on the host cores)."""
     import numpy as np
 
     import oracle
-    rows = 16
+    rows = 64
     xs = x[:rows]
     t = time.perf_counter()
     h = oracle.rmsnorm(xs, g, eps)

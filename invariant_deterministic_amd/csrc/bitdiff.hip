@@ -12,7 +12,10 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <typename T>
+// One workgroup per compared row pair.  VEC: the row is read as 16-byte
+// vectors (every load of a thread issued before any is used, so a row costs one
+// memory round trip); otherwise element by element.
+template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void row_bitdiff_kernel(
     const T *__restrict__ a, int64_t lda, const int64_t *__restrict__ a_rows,
     const T *__restrict__ b, int64_t ldb, const int64_t *__restrict__ b_rows, int64_t ncols,
@@ -23,10 +26,46 @@ __global__ __launch_bounds__(kThreads) void row_bitdiff_kernel(
   const T *pa = a + ra * lda;
   const T *pb = b + rb * ldb;
   unsigned long long bits = 0, elems = 0;
-  for (int64_t c = threadIdx.x; c < ncols; c += kThreads) {
-    const uint32_t d = (uint32_t)(pa[c] ^ pb[c]);
-    bits += (unsigned long long)__popc(d);
-    elems += d ? 1ull : 0ull;
+  if (VEC) {
+    constexpr int PER = 16 / sizeof(T);  // elements per 16-byte vector
+    const u32x4 *va = reinterpret_cast<const u32x4 *>(pa);
+    const u32x4 *vb = reinterpret_cast<const u32x4 *>(pb);
+    const int64_t nv = ncols / PER;
+    constexpr int U = 4;
+    for (int64_t c0 = threadIdx.x; c0 < nv; c0 += (int64_t)kThreads * U) {
+      u32x4 xa[U], xb[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + (int64_t)u * kThreads;
+        if (c < nv) {
+          xa[u] = va[c];
+          xb[u] = vb[c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + (int64_t)u * kThreads;
+        if (c < nv) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t d = xa[u][j] ^ xb[u][j];
+            bits += (unsigned long long)__popc(d);
+            if (sizeof(T) == 4) {
+              elems += d ? 1ull : 0ull;
+            } else {
+              elems += (d & 0xFFFFu) ? 1ull : 0ull;
+              elems += (d >> 16) ? 1ull : 0ull;
+            }
+          }
+        }
+      }
+    }
+  } else {
+    for (int64_t c = threadIdx.x; c < ncols; c += kThreads) {
+      const uint32_t d = (uint32_t)(pa[c] ^ pb[c]);
+      bits += (unsigned long long)__popc(d);
+      elems += d ? 1ull : 0ull;
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -68,11 +107,23 @@ extern "C" int bi_row_bitdiff(const void *a, int64_t lda, const int64_t *a_rows,
   if (nrows == 0) return BI_OK;
   hipStream_t s = (hipStream_t)stream;
   unsigned long long *c = reinterpret_cast<unsigned long long *>(counts);
-  if (elem_bytes == 2)
-    hipLaunchKernelGGL(row_bitdiff_kernel<uint16_t>, dim3((unsigned)nrows), dim3(kThreads), 0, s,
-                       (const uint16_t *)a, lda, a_rows, (const uint16_t *)b, ldb, b_rows, ncols, c);
-  else
-    hipLaunchKernelGGL(row_bitdiff_kernel<uint32_t>, dim3((unsigned)nrows), dim3(kThreads), 0, s,
-                       (const uint32_t *)a, lda, a_rows, (const uint32_t *)b, ldb, b_rows, ncols, c);
+  // 16-byte vectors when every row starts 16-byte aligned and holds whole vectors
+  const bool vec = ((uintptr_t)a % 16 == 0) && ((uintptr_t)b % 16 == 0) &&
+                   (lda * elem_bytes) % 16 == 0 && (ldb * elem_bytes) % 16 == 0 &&
+                   (ncols * elem_bytes) % 16 == 0;
+  const dim3 grid((unsigned)nrows), block(kThreads);
+  if (elem_bytes == 2) {
+    const uint16_t *pa = (const uint16_t *)a, *pb = (const uint16_t *)b;
+    if (vec)
+      hipLaunchKernelGGL((row_bitdiff_kernel<uint16_t, true>), grid, block, 0, s, pa, lda, a_rows, pb, ldb, b_rows, ncols, c);
+    else
+      hipLaunchKernelGGL((row_bitdiff_kernel<uint16_t, false>), grid, block, 0, s, pa, lda, a_rows, pb, ldb, b_rows, ncols, c);
+  } else {
+    const uint32_t *pa = (const uint32_t *)a, *pb = (const uint32_t *)b;
+    if (vec)
+      hipLaunchKernelGGL((row_bitdiff_kernel<uint32_t, true>), grid, block, 0, s, pa, lda, a_rows, pb, ldb, b_rows, ncols, c);
+    else
+      hipLaunchKernelGGL((row_bitdiff_kernel<uint32_t, false>), grid, block, 0, s, pa, lda, a_rows, pb, ldb, b_rows, ncols, c);
+  }
   return launch_status();
 }

@@ -21,9 +21,10 @@ def bi():
 
 
 @pytest.mark.parametrize("dtype,nbits", [(np.uint16, 16), (np.uint32, 32)])
-def test_bitdiff_matches_oracle_exactly(bi, dtype, nbits):
-    g = synth.rng(60 + nbits)
-    rows, cols = 37, 1000 + nbits      # ragged against 256 threads
+@pytest.mark.parametrize("cols", [1000, 1001, 4096])   # 16-byte vector path and element path
+def test_bitdiff_matches_oracle_exactly(bi, dtype, nbits, cols):
+    g = synth.rng(60 + nbits + cols)
+    rows = 37
     a = g.integers(0, 1 << nbits, size=(rows, cols), dtype=np.uint64).astype(dtype)
     b = a.copy()
     flips = g.integers(0, rows * cols, size=300)
