@@ -19,6 +19,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxChunks = 8;  // 16-byte chunks per thread: K <= 8 * 256 * 8
 
+// NCH: 16-byte chunks a thread may own (1, 2, 4 or 8), picked from K alone so
+// that the registers fit the row and nothing about the reduction changes.
+template <int NCH>
 __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
     const uint16_t *x, const uint16_t *__restrict__ w, uint16_t *y, int K,
     int64_t ldx, int64_t ldy, float eps) {
@@ -27,18 +30,24 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
   const int nchunks = K >> 3;
   const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + (int64_t)row * ldx);
 
-  u32x4 v[kMaxChunks];
+  // Issue every load of the row and of the weight before the reduction, so a
+  // workgroup spends one memory round trip, not two.
+  const u32x4 *wr = reinterpret_cast<const u32x4 *>(w);
+  u32x4 v[NCH], wv[NCH];
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int c = t + i * kThreads;
-    if (c < nchunks) v[i] = __builtin_nontemporal_load(xr + c);
+    if (c < nchunks) {
+      v[i] = __builtin_nontemporal_load(xr + c);
+      wv[i] = wr[c];
+    }
   }
 
   // Thread-local sum of squares in ascending element order.  Each square of a
   // bf16 value is exact in fp32, so only the additions round.
   float ss = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int c = t + i * kThreads;
     if (c < nchunks) {
 #pragma unroll
@@ -63,18 +72,16 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
   const float total = ((part[0] + part[1]) + part[2]) + part[3];
   const float r = 1.0f / sqrtf(total / (float)K + eps);
 
-  const u32x4 *wr = reinterpret_cast<const u32x4 *>(w);
   u32x4 *yr = reinterpret_cast<u32x4 *>(y + (int64_t)row * ldy);
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int c = t + i * kThreads;
     if (c < nchunks) {
-      const u32x4 wv = wr[c];
       u32x4 o;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float lo = (lo_bf16(v[i][j]) * r) * lo_bf16(wv[j]);
-        const float hi = (hi_bf16(v[i][j]) * r) * hi_bf16(wv[j]);
+        const float lo = (lo_bf16(v[i][j]) * r) * lo_bf16(wv[i][j]);
+        const float hi = (hi_bf16(v[i][j]) * r) * hi_bf16(wv[i][j]);
         o[j] = pack_bf16x2(lo, hi);
       }
       __builtin_nontemporal_store(o, yr + c);
@@ -101,7 +108,16 @@ extern "C" int bi_rmsnorm(const uint16_t *x, const uint16_t *w, uint16_t *y,
   const bool in_place = (x == y) && (ldx == ldy);
   if ((!in_place && overlap(sx, sy)) || overlap(sw, sy)) return BI_ERR_ALIAS;
   if (M == 0) return BI_OK;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3((unsigned)M), dim3(kThreads), 0,
-                     (hipStream_t)stream, x, w, y, (int)K, ldx, ldy, eps);
+  const int nch = (int)((K / 8 + kThreads - 1) / kThreads);
+  const dim3 grid((unsigned)M), block(kThreads);
+  hipStream_t st = (hipStream_t)stream;
+  if (nch <= 1)
+    hipLaunchKernelGGL(rmsnorm_kernel<1>, grid, block, 0, st, x, w, y, (int)K, ldx, ldy, eps);
+  else if (nch <= 2)
+    hipLaunchKernelGGL(rmsnorm_kernel<2>, grid, block, 0, st, x, w, y, (int)K, ldx, ldy, eps);
+  else if (nch <= 4)
+    hipLaunchKernelGGL(rmsnorm_kernel<4>, grid, block, 0, st, x, w, y, (int)K, ldx, ldy, eps);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<8>, grid, block, 0, st, x, w, y, (int)K, ldx, ldy, eps);
   return launch_status();
 }
