@@ -291,6 +291,19 @@ def sweep(path, bi, torch, dev, to_dev):
                          "config": bi.bi_gemm_config_id(N, K)})
             print(f"# sweep gemm K={K} N={N} M={M}: {recs[-1]['tflops']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
+            if M <= 64:
+                S = bi.bi_gemm_splitk_for(N, K)
+                ws = torch.empty(bi.bi_gemm_splitk_workspace_bytes(M, N, S), dtype=torch.uint8,
+                                 device=dev)
+                ms2 = _time_loop(torch, lambda i: bi.bi_gemm_splitk(xpool[:M], W, y=y, split_k=S,
+                                                                     ws=ws), n)
+                recs.append({"kernel": "bi_gemm_splitk", "K": K, "N": N, "M": M, "split_k": S,
+                             "us": ms2 * 1e3, "tflops": fl / (ms2 * 1e-3) / 1e12,
+                             "gbs": by / (ms2 * 1e-3) / 1e9,
+                             "frac_hbm": by / (ms2 * 1e-3) / 1e9 / PEAK_HBM_GBS})
+                print(f"# sweep gemm_splitk K={K} N={N} M={M} S={S}: {ms2*1e3:.1f} us "
+                      f"({recs[-1]['gbs']:.0f} GB/s) vs bi_gemm {ms*1e3:.1f} us",
+                      file=sys.stderr, flush=True)
         del W, xpool
     # RMSNorm over M (K = 4096), rotating buffers
     K = 4096

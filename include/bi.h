@@ -130,6 +130,57 @@ int bi_gemm_with_config(int config, const uint16_t *x, const uint16_t *w, uint16
                         int64_t ldx, int64_t ldw, int64_t ldy, void *stream);
 
 /*
+ * bi_gemm_splitk -- the same product with the K reduction split into split_k
+ * equal contiguous chunks, for batches too small to fill the chip with tiles.
+ *
+ * Defined by: "Cómo superar la no determinación en la inferencia de LLM",
+ * section "Multiplicación de matrices (matmul)": small batches need split-K
+ * for parallelism, and that breaks batch invariance when the split follows
+ * the batch size; keeping the split fixed keeps one reduction order.  The
+ * split here is the caller's fixed choice per layer (bi_gemm_splitk_for(N, K)
+ * gives one from (N, K) alone) and must not be chosen from M.
+ *
+ *   Same x, w, y, sizes and strides as bi_gemm; 1 <= split_k <= 64 and
+ *   K % (32 * split_k) == 0.
+ *   ws, ws_bytes: device fp32 workspace of at least
+ *       bi_gemm_splitk_workspace_bytes(M, N, split_k) bytes; on return it holds
+ *       the partial sums p_s[m][n] at ws[(s * M + m) * N + n].
+ * Reduction order of every output: chunk s covers k in [s*K/S, (s+1)*K/S),
+ * one ascending pass in 16-k steps (the bi_gemm main loop over that range);
+ * then bf16( (((p_0 + p_1) + p_2) + ...) + p_{S-1} ) in fp32, rounded to nearest
+ * even once.  split_k == 1 gives bi_gemm's bits.
+ */
+int bi_gemm_splitk(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                   int64_t M, int64_t N, int64_t K,
+                   int64_t ldx, int64_t ldw, int64_t ldy, int split_k,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* bi_gemm_splitk_workspace_bytes -- split_k * M * N * 4, rounded up to 256. */
+size_t bi_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int split_k);
+
+/* bi_gemm_splitk_for -- a split factor for (N, K) that fills the chip at M <= 64
+ * (a power of two, at least 4 K-stages per chunk), or -1 if (N, K) is not
+ * supported.  No M parameter, for the same reason as bi_gemm_config_id. */
+int bi_gemm_splitk_for(int64_t N, int64_t K);
+
+/*
+ * bi_gemm_mswitch_control -- CONTROL ONLY, NOT batch-invariant.  Picks the
+ * reduction from the batch size, the way a library tuned per shape does:
+ * bi_gemm_splitk(split_k = bi_gemm_splitk_for(N, K)) when 1 <= M <= 64, bi_gemm
+ * otherwise.  A row therefore gets different bits alone than inside a large
+ * batch.  This is the configuration switch of "Cómo superar la no
+ * determinación en la inferencia de LLM" (section "Multiplicación de matrices
+ * (matmul)") and the shape-driven source of drift named in the forum thread
+ * "You think you are measuring intelligence..." (second comment), kept to show
+ * that variation beside the atomic control.  ws as for bi_gemm_splitk (needed
+ * when M <= 64).
+ */
+int bi_gemm_mswitch_control(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                            int64_t M, int64_t N, int64_t K,
+                            int64_t ldx, int64_t ldw, int64_t ldy,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
  * bi_lora_shrink_workspace_bytes -- bytes of workspace bi_lora_shrink needs:
  * split_k * M * R * 4 (fp32 partials), rounded up to 256; 0 when split_k == 1.
  */

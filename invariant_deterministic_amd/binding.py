@@ -44,6 +44,12 @@ _lib_gemm_config_id = _sig("bi_gemm_config_id", [_i64, _i64])
 _lib_gemm_num_configs = _sig("bi_gemm_num_configs", [])
 _lib_gemm_with_config = _sig("bi_gemm_with_config",
                              [_int, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p])
+_lib_gemm_splitk = _sig("bi_gemm_splitk", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _int, _p,
+                                           ctypes.c_size_t, _p])
+_lib_gemm_splitk_ws = _sig("bi_gemm_splitk_workspace_bytes", [_i64, _i64, _int], ctypes.c_size_t)
+_lib_gemm_splitk_for = _sig("bi_gemm_splitk_for", [_i64, _i64])
+_lib_gemm_mswitch = _sig("bi_gemm_mswitch_control", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                     _p, ctypes.c_size_t, _p])
 _lib_ws_bytes = _sig("bi_lora_shrink_workspace_bytes", [_i64, _i64, _int], ctypes.c_size_t)
 _lib_shrink = _sig("bi_lora_shrink", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _int,
                                       _p, ctypes.c_size_t, _p])
@@ -55,7 +61,8 @@ _lib_row_bitdiff = _sig("bi_row_bitdiff", [_p, _i64, _p, _p, _i64, _p, _i64, _i6
 
 BI_OK = 0
 EXPORTS = ("bi_abi_version", "bi_status_str", "bi_rmsnorm", "bi_gemm", "bi_gemm_config_id",
-           "bi_gemm_num_configs", "bi_gemm_with_config", "bi_lora_shrink_workspace_bytes",
+           "bi_gemm_num_configs", "bi_gemm_with_config", "bi_gemm_splitk",
+           "bi_gemm_splitk_workspace_bytes", "bi_gemm_splitk_for", "bi_gemm_mswitch_control", "bi_lora_shrink_workspace_bytes",
            "bi_lora_shrink", "bi_lora_shrink_two_pass", "bi_lora_shrink_atomic", "bi_row_bitdiff")
 
 
@@ -164,6 +171,49 @@ def bi_gemm_with_config(config: int, x: torch.Tensor, w: torch.Tensor,
     _check(_lib_gemm_with_config(config, px, pw, py, M, N, K, ldx, ldw, ldy, _stream(stream)),
            "bi_gemm_with_config")
     return y
+
+
+def bi_gemm_splitk_workspace_bytes(M: int, N: int, split_k: int) -> int:
+    return int(_lib_gemm_splitk_ws(M, N, split_k))
+
+
+def bi_gemm_splitk_for(N: int, K: int) -> int:
+    return int(_lib_gemm_splitk_for(N, K))
+
+
+def _gemm_ws_call(fn, name, x, w, y, split_k, ws, stream):
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if ws is None:
+        need = bi_gemm_splitk_workspace_bytes(M, N, split_k if split_k else
+                                              max(1, bi_gemm_splitk_for(N, K)))
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    px, ldx = _mat(x, "x", _BF16_LIKE)
+    pw, ldw = _mat(w, "w", _BF16_LIKE)
+    py, ldy = _mat(y, "y", _BF16_LIKE)
+    args = [px, pw, py, M, N, K, ldx, ldw, ldy]
+    if split_k:
+        args.append(split_k)
+    _check(fn(*args, ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)), name)
+    return y
+
+
+def bi_gemm_splitk(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,
+                   split_k: int | None = None, ws: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """Split-K GEMM with a fixed split (default bi_gemm_splitk_for(N, K)) and a
+    fixed-order fp32 combine (see bi.h)."""
+    if split_k is None:
+        split_k = bi_gemm_splitk_for(w.shape[0], w.shape[1])
+    return _gemm_ws_call(_lib_gemm_splitk, "bi_gemm_splitk", x, w, y, split_k, ws, stream)
+
+
+def bi_gemm_mswitch_control(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,
+                            ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """CONTROL ONLY: chooses split-K from M (not batch-invariant)."""
+    return _gemm_ws_call(_lib_gemm_mswitch, "bi_gemm_mswitch_control", x, w, y, 0, ws, stream)
 
 
 def bi_lora_shrink_workspace_bytes(M: int, R: int, split_k: int) -> int:

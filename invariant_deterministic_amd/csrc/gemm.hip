@@ -184,32 +184,26 @@ __device__ __forceinline__ void wait_stages_after(int n) {
   else wait_vmcnt<0>();
 }
 
+// The K loop of one tile: x and w point at the first k of this tile's K range
+// and nkb stages of BK follow.  Leaves the tile's fp32 sums in acc.
 template <int BN, int BM>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
-    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+__device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[BN / 64][BM / 64], char *lds,
+                                              const uint16_t *__restrict__ x,
+                                              const uint16_t *__restrict__ w, int M, int N,
+                                              int nkb, int64_t ldx, int64_t ldw, int m0, int n0,
+                                              int wv, int lane) {
   using C = Cfg<BN, BM>;
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * C::STAGE];
-
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wv >> 1, wm = wv & 1;
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int n0 = tn * BN, m0 = tm * BM;
-
   LoadPlan<BN> pw;
   LoadPlan<BM> px;
   pw.init(n0, N, ldw, wv, lane);
   px.init(m0, M, ldx, wv, lane);
 
-  f32x16 acc[C::FN][C::FM];
 #pragma unroll
   for (int i = 0; i < C::FN; ++i)
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
 
-  const int nkb = K / BK;
   // Prologue: stages 0 .. kStages-1 in flight.
 #pragma unroll
   for (int s = 0; s < kStages; ++s) {
@@ -266,6 +260,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     mfma_step<BN, BM>(acc, f1);
   }
 
+}
+
+template <int BN, int BM>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+  using C = Cfg<BN, BM>;
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * C::STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wv >> 1, wm = wv & 1;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int n0 = tn * BN, m0 = tm * BM;
+
+  f32x16 acc[C::FN][C::FM];
+  gemm_mainloop<BN, BM>(acc, lds, x, w, M, N, K / BK, ldx, ldw, m0, n0, wv, lane);
+
   // Epilogue.  Accumulator block (i, j) of this wavefront, register v, holds
   // n = base_n + 8*(v/4) + 4*(lane/32) + v%4 and m = base_m + lane%32: four
   // consecutive n of one output row per group of 4 registers -> one 8-byte store.
@@ -290,6 +303,71 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   }
 }
 
+// Split-K partial tile: blockIdx.y = chunk s covers k in [s*kc, (s+1)*kc).
+// The same K loop as gemm_kernel over that range; the fp32 sums go to
+// ws[s][m][n] (row stride N), four consecutive n per 16-byte store.
+template <int BN, int BM>
+__global__ __launch_bounds__(kThreads, 1) void gemm_partial_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, float *__restrict__ ws,
+    int M, int N, int kc, int64_t ldx, int64_t ldw, int tiles_m, int tiles_n) {
+  using C = Cfg<BN, BM>;
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * C::STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wv >> 1, wm = wv & 1;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int n0 = tn * BN, m0 = tm * BM;
+  const int s = blockIdx.y;
+
+  f32x16 acc[C::FN][C::FM];
+  gemm_mainloop<BN, BM>(acc, lds, x + (int64_t)s * kc, w + (int64_t)s * kc, M, N, kc / BK, ldx,
+                        ldw, m0, n0, wv, lane);
+
+  float *part = ws + (int64_t)s * M * N;
+#pragma unroll
+  for (int j = 0; j < C::FM; ++j) {
+    const int m = m0 + wm * C::WM + j * 32 + (lane & 31);
+    if (m >= M) continue;
+    float *prow = part + (int64_t)m * N;
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * C::WN + i * 32 + q * 8 + (lane >> 5) * 4;
+        if (n < N) {
+          f32x4 o = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
+                     acc[i][j][q * 4 + 3]};
+          *reinterpret_cast<f32x4 *>(prow + n) = o;
+        }
+      }
+    }
+  }
+}
+
+// Fixed-order split-K combine: y[m][n] = bf16(((p_0 + p_1) + ...) + p_{S-1}),
+// eight outputs per thread.
+__global__ __launch_bounds__(kThreads) void gemm_splitk_combine_kernel(
+    const float *__restrict__ ws, uint16_t *__restrict__ y, int M, int N, int S, int64_t ldy) {
+  const int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  const int64_t total = (int64_t)M * N;
+  if (e >= total) return;
+  const int64_t m = e / N, n = e % N;
+  f32x4 a = *reinterpret_cast<const f32x4 *>(ws + e);
+  f32x4 b = *reinterpret_cast<const f32x4 *>(ws + e + 4);
+  for (int s = 1; s < S; ++s) {
+    a = a + *reinterpret_cast<const f32x4 *>(ws + (int64_t)s * total + e);
+    b = b + *reinterpret_cast<const f32x4 *>(ws + (int64_t)s * total + e + 4);
+  }
+  u32x4 o;
+  o[0] = pack_bf16x2(a[0], a[1]);
+  o[1] = pack_bf16x2(a[2], a[3]);
+  o[2] = pack_bf16x2(b[0], b[1]);
+  o[3] = pack_bf16x2(b[2], b[3]);
+  *reinterpret_cast<u32x4 *>(y + m * ldy + n) = o;
+}
+
 struct CfgEntry {
   int bn, bm;
   void (*kernel)(const uint16_t *, const uint16_t *, uint16_t *, int, int, int, int64_t,
@@ -303,6 +381,19 @@ const CfgEntry kConfigs[] = {
     {128, 256, gemm_kernel<128, 256>},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+
+// Split-K path: one tile shape for every (N, K) and M, sized for decode-like
+// batches (one 64-row tile covers M <= 64).
+constexpr int kSplitBN = 128, kSplitBM = 64;
+
+int splitk_for(int64_t N, int64_t K) {
+  const int64_t tiles_n = (N + kSplitBN - 1) / kSplitBN;
+  int S = 1;
+  // smallest power of two that gives >= 256 workgroups at M <= 64, keeping
+  // at least 4 stages of K per chunk
+  while (tiles_n * S < 256 && K % (2 * S * BK) == 0 && K / (2 * S) >= 4 * BK && S < 64) S *= 2;
+  return S;
+}
 
 int config_for(int64_t N, int64_t K) {
   (void)K;
@@ -364,4 +455,58 @@ extern "C" int bi_gemm_with_config(int config, const uint16_t *x, const uint16_t
   const int st = validate(x, w, y, M, N, K, ldx, ldw, ldy);
   if (st != BI_OK || M == 0) return st;
   return launch(config, x, w, y, M, N, K, ldx, ldw, ldy, stream);
+}
+
+extern "C" int bi_gemm_splitk_for(int64_t N, int64_t K) {
+  if (N < 8 || (N & 7) || K < BK || K % BK) return -1;
+  return splitk_for(N, K);
+}
+
+extern "C" size_t bi_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int split_k) {
+  if (M <= 0 || N <= 0 || split_k <= 0) return 0;
+  const size_t b = (size_t)split_k * (size_t)M * (size_t)N * 4u;
+  return (b + 255u) & ~(size_t)255u;
+}
+
+extern "C" int bi_gemm_splitk(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M,
+                              int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
+                              int split_k, void *ws, size_t ws_bytes, void *stream) {
+  int st = validate(x, w, y, M, N, K, ldx, ldw, ldy);
+  if (st != BI_OK) return st;
+  if (split_k < 1 || split_k > 64) return BI_ERR_UNSUPPORTED;
+  if (K % ((int64_t)split_k * BK)) return BI_ERR_SHAPE;
+  if (M == 0) return BI_OK;
+  if (!ws) return BI_ERR_NULL;
+  if (ws_bytes < bi_gemm_splitk_workspace_bytes(M, N, split_k)) return BI_ERR_WORKSPACE;
+  if (!aligned16(ws)) return BI_ERR_ALIGN;
+  const Span sw{(uintptr_t)ws, (uintptr_t)ws + (uintptr_t)(split_k * M * N * 4)};
+  if (overlap(sw, span_of(y, M, N, ldy, 2)) || overlap(sw, span_of(x, M, K, ldx, 2)) ||
+      overlap(sw, span_of(w, N, K, ldw, 2)))
+    return BI_ERR_ALIAS;
+  const int64_t tiles_m = (M + kSplitBM - 1) / kSplitBM, tiles_n = (N + kSplitBN - 1) / kSplitBN;
+  if (tiles_m * tiles_n > 0x7FFFFFFF) return BI_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  float *wsf = static_cast<float *>(ws);
+  hipLaunchKernelGGL((gemm_partial_kernel<kSplitBN, kSplitBM>),
+                     dim3((unsigned)(tiles_m * tiles_n), (unsigned)split_k), dim3(kThreads), 0, s,
+                     x, w, wsf, (int)M, (int)N, (int)(K / split_k), ldx, ldw, (int)tiles_m,
+                     (int)tiles_n);
+  if ((st = launch_status()) != BI_OK) return st;
+  const int64_t groups = (M * N / 8 + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(gemm_splitk_combine_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, wsf,
+                     y, (int)M, (int)N, split_k, ldy);
+  return launch_status();
+}
+
+extern "C" int bi_gemm_mswitch_control(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                                       int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw,
+                                       int64_t ldy, void *ws, size_t ws_bytes, void *stream) {
+  // CONTROL ONLY: the configuration switch batch-invariant kernels forbid --
+  // split-K when the batch is small, one pass otherwise.
+  if (M > 0 && M <= kSplitBM) {
+    const int S = bi_gemm_splitk_for(N, K);
+    if (S < 1) return BI_ERR_SHAPE;
+    return bi_gemm_splitk(x, w, y, M, N, K, ldx, ldw, ldy, S, ws, ws_bytes, stream);
+  }
+  return bi_gemm(x, w, y, M, N, K, ldx, ldw, ldy, stream);
 }

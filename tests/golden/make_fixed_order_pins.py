@@ -45,6 +45,14 @@ def pins():
     rows.append(("gemm_korder_ascending", 4096, nz, f32_bits(asc), bf16_bits_of_f32(asc)))
     rows.append(("gemm_korder_descending_is_wrong", 4096, nz, f32_bits(desc),
                  bf16_bits_of_f32(desc)))
+    # The same input through a fixed split-K of 2 (chunks [0, 2048), [2048, 4096)):
+    # each chunk folds its steps, then the partials fold in order.
+    p = []
+    for c in range(2):
+        t = np.array([x * w for k, x, w in k_terms if c * 2048 <= k < (c + 1) * 2048], np.float32)
+        p.append(oracle.combine_f32(t.reshape(-1, 1))[0] if len(t) else np.float32(0))
+    sk = oracle.combine_f32(np.array(p, np.float32).reshape(-1, 1))[0]
+    rows.append(("gemm_splitk2_korder", 4096, nz, f32_bits(sk), bf16_bits_of_f32(sk)))
 
     # LoRA shrink combine-order pin: K = 4096, split into 8 chunks of 512.
     s_terms = [(0, 1.0, 1.0), (512, 1.0, 2.0 ** -24), (1024, 1.0, 2.0 ** -24)]

@@ -35,6 +35,7 @@ class _Guarded:
 
     # position of the batch-size argument in each launching entry point
     M_ARG = {"bi_rmsnorm": 3, "bi_gemm": 3, "bi_gemm_with_config": 4, "bi_lora_shrink": 3,
+             "bi_gemm_splitk": 3, "bi_gemm_mswitch_control": 3,
              "bi_lora_shrink_two_pass": 3, "bi_lora_shrink_atomic": 3, "bi_row_bitdiff": 6}
 
     def __init__(self, lib):
@@ -67,6 +68,11 @@ def _load():
     L.bi_gemm.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, p]
     L.bi_gemm_with_config.argtypes = [i, p, p, p, i64, i64, i64, i64, i64, i64, p]
     L.bi_gemm_config_id.argtypes = [i64, i64]
+    L.bi_gemm_splitk.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i, p, ctypes.c_size_t, p]
+    L.bi_gemm_splitk_workspace_bytes.argtypes = [i64, i64, i]
+    L.bi_gemm_splitk_workspace_bytes.restype = ctypes.c_size_t
+    L.bi_gemm_splitk_for.argtypes = [i64, i64]
+    L.bi_gemm_mswitch_control.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, p, ctypes.c_size_t, p]
     L.bi_lora_shrink.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i, p, ctypes.c_size_t, p]
     L.bi_lora_shrink_two_pass.argtypes = L.bi_lora_shrink.argtypes
     L.bi_lora_shrink_atomic.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i, p]
@@ -149,6 +155,28 @@ def test_gemm_config_has_no_m_and_is_stable(lib):
     assert lib.bi_gemm_config_id(4096, 100) == -1
     assert lib.bi_gemm_config_id(4096, 96) >= 0
     assert lib.bi_gemm_config_id(4100, 4096) == -1
+
+
+def test_gemm_splitk_validation(lib):
+    f = lib.bi_gemm_splitk
+    need = lib.bi_gemm_splitk_workspace_bytes(4, 4096, 8)
+    assert need == 8 * 4 * 4096 * 4
+    a = (4, 4096, 4096, 4096, 4096, 4096)
+    assert f(X, W, Y, *a, 8, None, need, None) == BI_ERR_NULL
+    assert f(X, W, Y, *a, 8, WS, need - 1, None) == BI_ERR_WORKSPACE
+    assert f(X, W, Y, *a, 0, WS, need, None) == BI_ERR_UNSUPPORTED
+    assert f(X, W, Y, *a, 65, WS, need, None) == BI_ERR_UNSUPPORTED
+    assert f(X, W, Y, 4, 4096, 4064, 4064, 4064, 4096, 8, WS, need, None) == BI_ERR_SHAPE  # K % (32*8)
+    assert f(X, W, Y, *a, 8, Y + 64, need, None) == BI_ERR_ALIAS
+    assert f(X, W, Y, *a, 8, WS + 8, need, None) == BI_ERR_ALIGN
+    assert f(None, W, None, 0, 4096, 4096, 4096, 4096, 4096, 8, None, 0, None) == BI_OK
+    for N, K in ((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336), (28672, 8192)):
+        s = lib.bi_gemm_splitk_for(N, K)
+        assert s >= 1 and (s & (s - 1)) == 0 and K % (32 * s) == 0
+    assert lib.bi_gemm_splitk_for(4096, 4096) == 8 and lib.bi_gemm_splitk_for(1024, 4096) == 32
+    g = lib.bi_gemm_mswitch_control
+    assert g(X, W, Y, *a, None, need, None) == BI_ERR_NULL              # small M needs ws
+    assert g(X, W, Y, 0, 4096, 4096, 4096, 4096, 4096, None, 0, None) == BI_OK
 
 
 def test_shrink_validation(lib):

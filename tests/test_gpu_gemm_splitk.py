@@ -1,0 +1,150 @@
+"""GPU tests of the fixed split-K GEMM (bi_gemm_splitk) and of the M-switch
+control (bi_gemm_mswitch_control), against the fp64 oracle and the pins."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from invariant_deterministic_amd import synth, workloads
+from tests.gpu_util import check_bf16, check_f32, dev_bf16, host_f32, host_u16, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def bi():
+    need_gpu()
+    from invariant_deterministic_amd import binding
+    return binding
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, "fixed_order_pins.txt")) as f:
+        for ln in f:
+            if ln.startswith(name + " |"):
+                return [c.strip() for c in ln.split("|")]
+    raise KeyError(name)
+
+
+def _pin_inputs(name, rows=5, n=16, col=3):
+    row = _golden(name)
+    K = int(row[1])
+    x = np.zeros((rows, K), np.float32)
+    w = np.zeros((n, K), np.float32)
+    for term in row[2].split(","):
+        k, xv_w = term.split(":")
+        xv, wv = xv_w.split("*")
+        x[:, int(k)] = float(xv)
+        w[col, int(k)] = float(wv)
+    return synth.f32_to_bf16_bits(x), synth.f32_to_bf16_bits(w), row
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1024, 1024), (37, 520, 4096), (64, 4096, 4096),
+                                   (130, 264, 14336)])
+def test_splitk_integer_inputs_bitwise(bi, M, N, K):
+    x = synth.int_bf16((M, K), M + 7, -4, 4)
+    w = synth.int_bf16((N, K), N + 7, -4, 4)
+    want = oracle.bf16_round(oracle.gemm(x, w))
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    for S in (1, 2, 4, 8):
+        if K % (32 * S):
+            continue
+        say(f"splitk int M={M} N={N} K={K} S={S}")
+        assert np.array_equal(host_u16(bi.bi_gemm_splitk(X, Wt, split_k=S)), want), S
+
+
+def test_splitk_one_equals_bi_gemm(bi):
+    x = synth.normal_bf16((70, 4096), 301)
+    w = synth.normal_bf16((1032, 4096), 302, std=0.02)
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    assert np.array_equal(host_u16(bi.bi_gemm_splitk(X, Wt, split_k=1)), host_u16(bi.bi_gemm(X, Wt)))
+
+
+def test_splitk_k_order_pin(bi):
+    """split 2: the chunk partials fold in order to 1 + 2^-8 + 2^-23 -> 0x3F81
+    (one pass gives 0x3F80)."""
+    x, w, row = _pin_inputs("gemm_splitk2_korder")
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    y = host_u16(bi.bi_gemm_splitk(X, Wt, split_k=2))
+    assert np.all(y[:, 3] == int(row[4], 16)), [hex(v) for v in y[:, 3]]
+    y1 = host_u16(bi.bi_gemm(X, Wt))
+    assert np.all(y1[:, 3] == int(_golden("gemm_korder_ascending")[4], 16))
+    check_bf16(y, oracle.gemm(x, w), "split-2 pin within tolerance")
+
+
+def test_splitk_partials_and_exact_combine(bi):
+    """Each fp32 partial matches the oracle over its chunk; y is bit-exactly the
+    oracle's fp32 fold of the partials rounded to bf16."""
+    M, N, K, S = 33, 1024, 4096, 4
+    x = synth.normal_bf16((M, K), 303)
+    w = synth.normal_bf16((N, K), 304, std=0.02)
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    ws = torch.zeros(bi.bi_gemm_splitk_workspace_bytes(M, N, S), dtype=torch.uint8, device="cuda")
+    y = host_u16(bi.bi_gemm_splitk(X, Wt, split_k=S, ws=ws))
+    p = host_f32(ws.view(torch.float32)[: S * M * N]).reshape(S, M, N)
+    kc = K // S
+    for s in range(S):
+        check_f32(p[s], oracle.gemm(x[:, s * kc:(s + 1) * kc].copy(), w[:, s * kc:(s + 1) * kc].copy()),
+                  f"partial {s}")
+    fold = oracle.combine_f32(p)
+    assert np.array_equal(y, oracle.bf16_round(fold.astype(np.float64)))
+
+
+@pytest.mark.parametrize("shape_index", [0, 1, 2, 3])
+def test_splitk_parity_small_m(bi, shape_index):
+    c = workloads.LLAMA8B
+    K, N = c["shapes"][shape_index]
+    x = workloads.llama8b_x(K, rows=64)
+    w = workloads.llama8b_w(shape_index)
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    S = bi.bi_gemm_splitk_for(N, K)
+    for M in (1, 5, 64):
+        say(f"splitk parity K={K} N={N} M={M} S={S}")
+        check_bf16(host_u16(bi.bi_gemm_splitk(X[:M], Wt, split_k=S)), oracle.gemm(x[:M], w),
+                   f"K={K} N={N} M={M}")
+
+
+def test_splitk_batch_invariance(bi):
+    """The split is fixed by (N, K): rows agree bitwise alone and in batches up
+    to M = 1000, prefix and permuted."""
+    from invariant_deterministic_amd import harness
+    K, N = 4096, 4096
+    x = workloads.llama8b_x(K, rows=1024)
+    X = dev_bf16(x)
+    Wt = dev_bf16(workloads.llama8b_w(0))
+    S = bi.bi_gemm_splitk_for(N, K)
+    perm = torch.from_numpy(synth.permutation(1024, 305))
+    batches = harness.prefix_and_permuted_batches((1, 2, 7, 64, 65, 127, 1000), 1024, perm, "cuda")
+    r = harness.batch_invariance(lambda xb: bi.bi_gemm_splitk(xb, Wt, split_k=S), X,
+                                 [0, 1, 6, 63, 64, 126, 999], batches)
+    assert r["rows"] > 10 and r["diff_bits"] == 0, r
+
+
+def test_mswitch_control_breaks_invariance(bi):
+    """The control picks split-K for M <= 64 and one pass above.  At N = 16384
+    its split is 2, so the pinned row reads 0x3F81 alone and 0x3F80 inside a
+    batch of 128; random rows differ too.  bi_gemm and bi_gemm_splitk give every
+    row one answer at any batch size."""
+    N, K = 16384, 4096
+    assert bi.bi_gemm_splitk_for(N, K) == 2
+    xp, wp, row = _pin_inputs("gemm_splitk2_korder", rows=1, n=4)
+    x = synth.normal_bf16((128, K), 306)
+    x[0] = xp[0]
+    w = synth.normal_bf16((N, K), 307, std=0.02)
+    w[3] = wp[3]
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    solo = np.stack([host_u16(bi.bi_gemm_mswitch_control(X[i:i + 1], Wt))[0] for i in range(64)])
+    batch = host_u16(bi.bi_gemm_mswitch_control(X, Wt))[:64]
+    assert solo[0, 3] == int(_golden("gemm_splitk2_korder")[4], 16)
+    assert batch[0, 3] == int(_golden("gemm_korder_ascending")[4], 16)
+    diff_elems = int((solo != batch).sum())
+    say(f"mswitch control: {diff_elems} of {solo.size} outputs differ alone vs in a batch of 128")
+    assert diff_elems > 1
+    for fn in (lambda xb: bi.bi_gemm(xb, Wt), lambda xb: bi.bi_gemm_splitk(xb, Wt, split_k=2)):
+        s1 = np.stack([host_u16(fn(X[i:i + 1]))[0] for i in range(8)])
+        assert np.array_equal(s1, host_u16(fn(X))[:8])
