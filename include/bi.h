@@ -241,6 +241,41 @@ int bi_lora_shrink_atomic(const uint16_t *x, const uint16_t *a, float *y,
                           void *stream);
 
 /*
+ * bi_decode_attention -- batch-invariant decode attention with a fixed split
+ * size: o[b][h] = sum_t softmax_t(q[b][h] . k[b][t][h/G] / sqrt(D)) v[b][t][h/G].
+ *
+ * Defined by: "Cómo superar la no determinación en la inferencia de LLM",
+ * section "Attention": parallel over queries, each query's keys/values reduced
+ * in one order; a split-KV reduction fixes the split *size*, not the number of
+ * splits; cache and new tokens share one key/value layout.
+ *
+ *   q        [B, H, D] bf16, contiguous (one decode query per sequence)
+ *   k_cache, v_cache  [B, Tmax, Hkv, D] bf16, contiguous; the new token's key
+ *            and value are already written at position lens[b] - 1.
+ *   lens     [B] int32 on the device: tokens of sequence b, in [1, Tmax]
+ *            (values outside are clamped into that range).
+ *   o        [B, H, D] bf16 output.
+ *   D in {64, 128}; H % Hkv == 0 and H / Hkv <= 8 (grouped-query heads);
+ *   split_size (tokens per chunk) in {128, 256, 512}: a constant of the
+ *   deployment, never derived from the batch.
+ *   ws, ws_bytes: fp32 workspace of bi_decode_attention_workspace_bytes(B, H,
+ *   Tmax, D, split_size) bytes (per-chunk max, sum and weighted values).
+ * Order of every output: per chunk of split_size tokens, scores with d
+ * ascending, max, exp, a sum in a fixed lane/xor order, values with t
+ * ascending; chunks folded with c ascending (see attention.hip).  The result
+ * for sequence b depends on its own q, cache and length only.
+ */
+int bi_decode_attention(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                        const int32_t *lens, uint16_t *o,
+                        int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t Tmax,
+                        int split_size, void *ws, size_t ws_bytes, void *stream);
+
+/* bi_decode_attention_workspace_bytes -- B * H * ceil(Tmax / split_size) *
+ * (D + 2) * 4, rounded up to 256. */
+size_t bi_decode_attention_workspace_bytes(int64_t B, int64_t H, int64_t Tmax, int64_t D,
+                                           int split_size);
+
+/*
  * bi_row_bitdiff -- bitwise comparison of rows, the invariance check.
  *
  * Defined by: "God Does Not Play Dice: Enforcing Batch Invariance in Agentic

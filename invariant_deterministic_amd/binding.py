@@ -50,6 +50,10 @@ _lib_gemm_splitk_ws = _sig("bi_gemm_splitk_workspace_bytes", [_i64, _i64, _int],
 _lib_gemm_splitk_for = _sig("bi_gemm_splitk_for", [_i64, _i64])
 _lib_gemm_mswitch = _sig("bi_gemm_mswitch_control", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
                                                      _p, ctypes.c_size_t, _p])
+_lib_attn = _sig("bi_decode_attention", [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _int, _p,
+                                         ctypes.c_size_t, _p])
+_lib_attn_ws = _sig("bi_decode_attention_workspace_bytes", [_i64, _i64, _i64, _i64, _int],
+                    ctypes.c_size_t)
 _lib_ws_bytes = _sig("bi_lora_shrink_workspace_bytes", [_i64, _i64, _int], ctypes.c_size_t)
 _lib_shrink = _sig("bi_lora_shrink", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _int,
                                       _p, ctypes.c_size_t, _p])
@@ -63,7 +67,8 @@ BI_OK = 0
 EXPORTS = ("bi_abi_version", "bi_status_str", "bi_rmsnorm", "bi_gemm", "bi_gemm_config_id",
            "bi_gemm_num_configs", "bi_gemm_with_config", "bi_gemm_splitk",
            "bi_gemm_splitk_workspace_bytes", "bi_gemm_splitk_for", "bi_gemm_mswitch_control", "bi_lora_shrink_workspace_bytes",
-           "bi_lora_shrink", "bi_lora_shrink_two_pass", "bi_lora_shrink_atomic", "bi_row_bitdiff")
+           "bi_lora_shrink", "bi_lora_shrink_two_pass", "bi_lora_shrink_atomic", "bi_row_bitdiff",
+           "bi_decode_attention", "bi_decode_attention_workspace_bytes")
 
 
 class BiError(RuntimeError):
@@ -301,3 +306,34 @@ def bi_row_bitdiff(a: torch.Tensor, b: torch.Tensor, a_rows: torch.Tensor | None
                             nrows, ncols, a.element_size(), counts.data_ptr(), _stream(stream)),
            "bi_row_bitdiff")
     return counts
+
+
+def bi_decode_attention_workspace_bytes(B: int, H: int, Tmax: int, D: int, split_size: int) -> int:
+    return int(_lib_attn_ws(B, H, Tmax, D, split_size))
+
+
+def bi_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        lens: torch.Tensor, o: torch.Tensor | None = None, split_size: int = 256,
+                        ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Batch-invariant decode attention (see bi.h).  q [B, H, D]; caches
+    [B, Tmax, Hkv, D]; lens int32 [B] on the device."""
+    B, H, D = q.shape
+    Bk, Tmax, Hkv, Dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or Bk != B or Dk != D:
+        raise ValueError("cache shapes do not match q")
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if not t.is_cuda or t.dtype not in _BF16_LIKE or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor")
+    if lens.dtype != torch.int32 or not lens.is_cuda or tuple(lens.shape) != (B,):
+        raise ValueError("lens must be a device int32 vector of B lengths")
+    if o is None:
+        o = torch.empty((B, H, D), dtype=q.dtype, device=q.device)
+    if not o.is_contiguous() or tuple(o.shape) != (B, H, D):
+        raise ValueError("o must be a contiguous [B, H, D] tensor")
+    need = bi_decode_attention_workspace_bytes(B, H, Tmax, D, split_size)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(_lib_attn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lens.data_ptr(),
+                     o.data_ptr(), B, H, Hkv, D, Tmax, split_size, ws.data_ptr(),
+                     ws.numel() * ws.element_size(), _stream(stream)), "bi_decode_attention")
+    return o

@@ -58,9 +58,11 @@ def lib() -> ctypes.CDLL:
                                      ctypes.c_int]
         L.oracle_combine_f32.argtypes = [p, i64, i64, p]
         L.oracle_bitdiff.argtypes = [p, p, i64, ctypes.c_int, p]
+        L.oracle_decode_attention.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, ctypes.c_int]
         L.oracle_max_threads.restype = ctypes.c_int
         for f in (L.oracle_bf16_decode, L.oracle_bf16_round, L.oracle_gemm,
-                  L.oracle_rmsnorm, L.oracle_combine_f32, L.oracle_bitdiff):
+                  L.oracle_rmsnorm, L.oracle_combine_f32, L.oracle_bitdiff,
+                  L.oracle_decode_attention):
             f.restype = None
         _lib = L
     return _lib
@@ -128,6 +130,23 @@ def rmsnorm(x, w, eps: float, threads: int = 0) -> np.ndarray:
     y = np.empty((M, K), dtype=np.float64)
     lib().oracle_rmsnorm(_ptr(x), K, _ptr(w), _ptr(y), K, M, K, float(eps), threads)
     return y
+
+
+def decode_attention(q, k, v, lens, threads: int = 0) -> np.ndarray:
+    """fp64 decode attention.  q [B, H, D], k and v [B, Tmax, Hkv, D] (bf16
+    bits), lens [B] valid tokens per sequence -> o [B, H, D]."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    B, H, D = q.shape
+    Bk, Tmax, Hkv, Dk = k.shape
+    if k.shape != v.shape or Bk != B or Dk != D or H % Hkv or lens.shape != (B,):
+        raise ValueError("shape mismatch")
+    if np.any(lens < 1) or np.any(lens > Tmax):
+        raise ValueError("lengths must be in [1, Tmax]")
+    o = np.empty((B, H, D), dtype=np.float64)
+    lib().oracle_decode_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(lens), _ptr(o), B, H, Hkv, D,
+                                  Tmax, threads)
+    return o
 
 
 def combine_f32(partials) -> np.ndarray:

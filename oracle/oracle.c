@@ -29,6 +29,13 @@
  *       order used by the product is the left fold over s = 0..S-1 in fp32;
  *       this is that definition, in fp32, because its point is the exact bits.
  *
+ *   Decode attention  o[b][h] = sum_t softmax_t(q.k_t / sqrt(D)) v_t
+ *       Same summary, section "Attention": one query token per sequence
+ *       attends to every cached key/value of its own sequence (the new token
+ *       already appended to the cache, one layout for both).  Query head h
+ *       reads key/value head h / (H / Hkv).  Scores, softmax and the weighted
+ *       sum in fp64, unrounded; exp from libm.
+ *
  *   Bit differences  popcount(a XOR b), and the count of differing elements.
  *       The check that "God Does Not Play Dice: Enforcing Batch Invariance in
  *       Agentic Kernel Generation" (abstract) asks for: bitwise consistency of
@@ -176,6 +183,55 @@ void oracle_combine_f32(const float *p, int64_t S, int64_t n, float *out)
             acc = acc + p[s * n + e];
         out[e] = acc;
     }
+}
+
+/* ---------------------------------------------------- decode attention ---- */
+
+/* q [B][H][D], k and v [B][Tmax][Hkv][D] (bf16), lens[b] valid tokens of
+ * sequence b; o [B][H][D] in fp64. */
+void oracle_decode_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const int32_t *lens, double *o, int64_t B, int64_t H,
+                             int64_t Hkv, int64_t D, int64_t Tmax, int threads)
+{
+    const int64_t G = H / Hkv;
+#ifdef _OPENMP
+    if (threads <= 0)
+        threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(threads) collapse(2)
+#endif
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t kh = h / G;
+            const int64_t T = lens[b];
+            const double scale = 1.0 / sqrt((double)D);
+            double mx = -INFINITY;
+            for (int64_t t = 0; t < T; ++t) {
+                double s = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    s += bf16_value(q[(b * H + h) * D + d]) *
+                         bf16_value(k[((b * Tmax + t) * Hkv + kh) * D + d]);
+                s *= scale;
+                if (s > mx)
+                    mx = s;
+            }
+            double l = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                o[(b * H + h) * D + d] = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                double s = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    s += bf16_value(q[(b * H + h) * D + d]) *
+                         bf16_value(k[((b * Tmax + t) * Hkv + kh) * D + d]);
+                const double p = exp(s * scale - mx);
+                l += p;
+                for (int64_t d = 0; d < D; ++d)
+                    o[(b * H + h) * D + d] += p * bf16_value(v[((b * Tmax + t) * Hkv + kh) * D + d]);
+            }
+            for (int64_t d = 0; d < D; ++d)
+                o[(b * H + h) * D + d] /= l;
+        }
+    }
+    (void)threads;
 }
 
 /* ------------------------------------------------------- bit differences ---- */

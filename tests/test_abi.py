@@ -35,7 +35,7 @@ class _Guarded:
 
     # position of the batch-size argument in each launching entry point
     M_ARG = {"bi_rmsnorm": 3, "bi_gemm": 3, "bi_gemm_with_config": 4, "bi_lora_shrink": 3,
-             "bi_gemm_splitk": 3, "bi_gemm_mswitch_control": 3,
+             "bi_gemm_splitk": 3, "bi_gemm_mswitch_control": 3, "bi_decode_attention": 5,
              "bi_lora_shrink_two_pass": 3, "bi_lora_shrink_atomic": 3, "bi_row_bitdiff": 6}
 
     def __init__(self, lib):
@@ -79,6 +79,9 @@ def _load():
     L.bi_lora_shrink_workspace_bytes.argtypes = [i64, i64, i]
     L.bi_lora_shrink_workspace_bytes.restype = ctypes.c_size_t
     L.bi_row_bitdiff.argtypes = [p, i64, p, p, i64, p, i64, i64, i, p, p]
+    L.bi_decode_attention.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i, p, ctypes.c_size_t, p]
+    L.bi_decode_attention_workspace_bytes.argtypes = [i64, i64, i64, i64, i]
+    L.bi_decode_attention_workspace_bytes.restype = ctypes.c_size_t
     L.bi_status_str.restype = ctypes.c_char_p
     return L
 
@@ -213,3 +216,20 @@ def test_bitdiff_validation(lib):
     assert f(X, 4, None, Y, 8, None, 1, 8, 2, WS, None) == BI_ERR_SHAPE
     assert f(X + 1, 8, None, Y, 8, None, 1, 8, 2, WS, None) == BI_ERR_ALIGN
     assert f(X, 8, None, Y, 8, None, 0, 8, 2, WS, None) == BI_OK
+
+
+def test_decode_attention_validation(lib):
+    f = lib.bi_decode_attention
+    need = lib.bi_decode_attention_workspace_bytes(2, 32, 1000, 128, 256)
+    assert need == (2 * 32 * 4 * 130 * 4 + 255) // 256 * 256
+    L = WS + (1 << 24)
+    a = (2, 32, 8, 128, 1000)
+    assert f(X, W, Y, L, None, *a, 256, WS, need, None) == BI_ERR_NULL
+    assert f(X, W, Y, L, X + (1 << 26), 2, 32, 8, 96, 1000, 256, WS, need, None) == BI_ERR_UNSUPPORTED
+    assert f(X, W, Y, L, X + (1 << 26), 2, 32, 3, 128, 1000, 256, WS, need, None) == BI_ERR_UNSUPPORTED
+    assert f(X, W, Y, L, X + (1 << 26), 2, 32, 2, 128, 1000, 256, WS, need, None) == BI_ERR_UNSUPPORTED  # G=16
+    assert f(X, W, Y, L, X + (1 << 26), *a, 100, WS, need, None) == BI_ERR_UNSUPPORTED
+    assert f(X, W, Y, L + 2, X + (1 << 26), *a, 256, WS, need, None) == BI_ERR_ALIGN
+    assert f(X, W, Y, L, X + (1 << 26), *a, 256, WS, need - 1, None) == BI_ERR_WORKSPACE
+    assert f(X, W, Y, L, X, *a, 256, WS, need, None) == BI_ERR_ALIAS
+    assert f(None, None, None, None, None, 0, 32, 8, 128, 1000, 256, None, 0, None) == BI_OK

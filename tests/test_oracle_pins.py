@@ -439,3 +439,85 @@ def test_bitdiff_random_against_python_popcount():
     bits = sum(bin(int(x) ^ int(y)).count("1") for x, y in zip(a, b))
     elems = sum(1 for x, y in zip(a, b) if x != y)
     assert oracle.bitdiff(a, b) == (bits, elems)
+
+
+# ------------------------------------------------------- decode attention --
+
+def _attn_exact(q, k, v, lens, digits=50):
+    """Brute-force decode attention with 50-digit decimals (exact dot products,
+    decimal exp), for tiny sizes."""
+    ctx = decimal.Context(prec=digits)
+    B, H, D = q.shape
+    _, Tmax, Hkv, _ = k.shape
+    G = H // Hkv
+    dec = lambda h: (lambda f: ctx.divide(decimal.Decimal(f.numerator), decimal.Decimal(f.denominator)))(bf16_fraction(int(h)))
+    out = np.zeros((B, H, D))
+    for b in range(B):
+        for h in range(H):
+            kh = h // G
+            scale = ctx.divide(decimal.Decimal(1), ctx.sqrt(decimal.Decimal(D)))
+            s = []
+            for t in range(int(lens[b])):
+                acc = decimal.Decimal(0)
+                for d in range(D):
+                    acc = ctx.add(acc, ctx.multiply(dec(q[b, h, d]), dec(k[b, t, kh, d])))
+                s.append(ctx.multiply(acc, scale))
+            mx = max(s)
+            p = [ctx.exp(ctx.subtract(x, mx)) for x in s]
+            l = sum(p, decimal.Decimal(0))
+            for d in range(D):
+                num = sum((ctx.multiply(p[t], dec(v[b, t, kh, d])) for t in range(len(p))), decimal.Decimal(0))
+                out[b, h, d] = float(ctx.divide(num, l))
+    return out
+
+
+def test_attention_brute_force_small():
+    """B=2, H=4 query heads over Hkv=2 key/value heads (groups of 2), D=4,
+    ragged lengths 3 and 5: against 50-digit decimal arithmetic."""
+    q = random_bf16_wide((2, 4, 4), 501, binades=2)
+    k = random_bf16_wide((2, 6, 2, 4), 502, binades=2)
+    v = random_bf16_wide((2, 6, 2, 4), 503, binades=3)
+    lens = np.array([3, 5], np.int32)
+    o = oracle.decode_attention(q, k, v, lens)
+    ex = _attn_exact(q, k, v, lens)
+    assert np.allclose(o, ex, rtol=1e-13, atol=1e-13 * np.abs(ex).max())
+
+
+def test_attention_single_token_is_value():
+    q = synth.normal_bf16((3, 8, 64), 504)
+    k = synth.normal_bf16((3, 4, 2, 64), 505)
+    v = synth.normal_bf16((3, 4, 2, 64), 506)
+    o = oracle.decode_attention(q, k, v, np.ones(3, np.int32))
+    vd = oracle.bf16_decode(v)
+    for h in range(8):
+        assert np.array_equal(o[:, h], vd[:, 0, h // 4])
+
+
+def test_attention_uniform_keys_average_values():
+    """Equal keys give equal weights: the output is the plain mean of V."""
+    B, H, Hkv, D, T = 2, 4, 4, 32, 37
+    q = synth.normal_bf16((B, H, D), 507)
+    k = np.broadcast_to(synth.normal_bf16((1, 1, Hkv, D), 508), (B, T, Hkv, D)).copy()
+    v = synth.normal_bf16((B, T, Hkv, D), 509)
+    o = oracle.decode_attention(q, k, v, np.full(B, T, np.int32))
+    mean = oracle.bf16_decode(v).mean(axis=1)          # [B, Hkv, D]
+    assert np.allclose(o, mean, rtol=1e-13, atol=1e-15)
+
+
+def test_attention_dominant_key_and_masked_tail():
+    """One key far above the rest selects its value; positions past a
+    sequence's length (filled with NaN) are never read."""
+    B, H, D, Tmax = 2, 2, 16, 9
+    q = synth.f32_to_bf16_bits(np.ones((B, H, D), np.float32))
+    k = synth.normal_bf16((B, Tmax, H, D), 510, std=0.01)
+    k[:, 2] = synth.f32_to_bf16_bits(np.full((B, H, D), 8.0, np.float32))   # score 8*16/4 = 32
+    v = synth.normal_bf16((B, Tmax, H, D), 511)
+    lens = np.array([5, 3], np.int32)
+    k[0, 5:] = 0x7FC0
+    v[0, 5:] = 0x7FC0
+    k[1, 3:] = 0x7FC0
+    v[1, 3:] = 0x7FC0
+    o = oracle.decode_attention(q, k, v, lens)
+    assert np.all(np.isfinite(o))
+    vd = oracle.bf16_decode(v)
+    assert np.allclose(o[:, :, :], vd[:, 2, :, :], rtol=0, atol=1e-12 * 8)
