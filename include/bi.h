@@ -276,6 +276,27 @@ size_t bi_decode_attention_workspace_bytes(int64_t B, int64_t H, int64_t Tmax, i
                                            int split_size);
 
 /*
+ * bi_lora_expand -- LoRA expand: y[m][n] = bf16( base[m][n] + scale * sum_r l[m][r] * b[n][r] ).
+ *
+ * Defined by: "Reproducible LoRA Inference Through Deterministic Split-K
+ * Reduction", abstract: the low-rank LoRA multiplications; the fp32 shrink
+ * output feeds this one.
+ *
+ *   l     [M, R] fp32, row stride ldl (the shrink output)
+ *   b     [N, R] bf16, row stride ldb (LoRA up-projection, R-contiguous)
+ *   base  [M, N] bf16, row stride ldbase, or NULL (then 0); may equal y when
+ *         ldbase == ldy (in-place add)
+ *   y     [M, N] bf16, row stride ldy
+ *   R == 16; N >= 8, N % 8 == 0, N <= 2^23; ldy, ldbase % 8 == 0.
+ * Order of every output: products summed in ascending r in fp32, the sum
+ * multiplied by scale, added to base in fp32, rounded to nearest even once.
+ */
+int bi_lora_expand(const float *l, const uint16_t *b, const uint16_t *base, uint16_t *y,
+                   int64_t M, int64_t N, int64_t R,
+                   int64_t ldl, int64_t ldb, int64_t ldbase, int64_t ldy, float scale,
+                   void *stream);
+
+/*
  * bi_row_bitdiff -- bitwise comparison of rows, the invariance check.
  *
  * Defined by: "God Does Not Play Dice: Enforcing Batch Invariance in Agentic

@@ -54,6 +54,8 @@ _lib_attn = _sig("bi_decode_attention", [_p, _p, _p, _p, _p, _i64, _i64, _i64, _
                                          ctypes.c_size_t, _p])
 _lib_attn_ws = _sig("bi_decode_attention_workspace_bytes", [_i64, _i64, _i64, _i64, _int],
                     ctypes.c_size_t)
+_lib_expand = _sig("bi_lora_expand", [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                      ctypes.c_float, _p])
 _lib_ws_bytes = _sig("bi_lora_shrink_workspace_bytes", [_i64, _i64, _int], ctypes.c_size_t)
 _lib_shrink = _sig("bi_lora_shrink", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _int,
                                       _p, ctypes.c_size_t, _p])
@@ -68,7 +70,7 @@ EXPORTS = ("bi_abi_version", "bi_status_str", "bi_rmsnorm", "bi_gemm", "bi_gemm_
            "bi_gemm_num_configs", "bi_gemm_with_config", "bi_gemm_splitk",
            "bi_gemm_splitk_workspace_bytes", "bi_gemm_splitk_for", "bi_gemm_mswitch_control", "bi_lora_shrink_workspace_bytes",
            "bi_lora_shrink", "bi_lora_shrink_two_pass", "bi_lora_shrink_atomic", "bi_row_bitdiff",
-           "bi_decode_attention", "bi_decode_attention_workspace_bytes")
+           "bi_decode_attention", "bi_decode_attention_workspace_bytes", "bi_lora_expand")
 
 
 class BiError(RuntimeError):
@@ -337,3 +339,20 @@ def bi_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
                      o.data_ptr(), B, H, Hkv, D, Tmax, split_size, ws.data_ptr(),
                      ws.numel() * ws.element_size(), _stream(stream)), "bi_decode_attention")
     return o
+
+
+def bi_lora_expand(l: torch.Tensor, b: torch.Tensor, base: torch.Tensor | None = None,
+                   y: torch.Tensor | None = None, scale: float = 1.0,
+                   stream=None) -> torch.Tensor:
+    """y = bf16(base + scale * l . b^T), l fp32 [M, R], b bf16 [N, R] (see bi.h)."""
+    M, R = l.shape
+    N = b.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=l.device)
+    pl, ldl = _mat(l, "l", (torch.float32,))
+    pb, ldb = _mat(b, "b", _BF16_LIKE)
+    py, ldy = _mat(y, "y", _BF16_LIKE)
+    pbase, ldbase = (None, 0) if base is None else _mat(base, "base", _BF16_LIKE)
+    _check(_lib_expand(pl, pb, pbase, py, M, N, R, ldl, ldb, ldbase, ldy, float(scale),
+                       _stream(stream)), "bi_lora_expand")
+    return y

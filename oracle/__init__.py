@@ -59,10 +59,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_combine_f32.argtypes = [p, i64, i64, p]
         L.oracle_bitdiff.argtypes = [p, p, i64, ctypes.c_int, p]
         L.oracle_decode_attention.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, ctypes.c_int]
+        L.oracle_lora_expand.argtypes = [p, p, p, p, i64, i64, i64, ctypes.c_double]
         L.oracle_max_threads.restype = ctypes.c_int
         for f in (L.oracle_bf16_decode, L.oracle_bf16_round, L.oracle_gemm,
                   L.oracle_rmsnorm, L.oracle_combine_f32, L.oracle_bitdiff,
-                  L.oracle_decode_attention):
+                  L.oracle_decode_attention, L.oracle_lora_expand):
             f.restype = None
         _lib = L
     return _lib
@@ -147,6 +148,26 @@ def decode_attention(q, k, v, lens, threads: int = 0) -> np.ndarray:
     lib().oracle_decode_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(lens), _ptr(o), B, H, Hkv, D,
                                   Tmax, threads)
     return o
+
+
+def lora_expand(l, b, base=None, scale: float = 1.0) -> np.ndarray:
+    """fp64 ``y[m, n] = base[m, n] + scale * sum_r l[m, r] * b[n, r]`` with fp32
+    ``l [M, R]``, bf16 ``b [N, R]``, optional bf16 ``base [M, N]``."""
+    l = np.ascontiguousarray(l, dtype=np.float32)
+    b = _u16(b)
+    M, R = l.shape
+    N = b.shape[0]
+    if b.shape != (N, R):
+        raise ValueError("shape mismatch")
+    bp = 0
+    if base is not None:
+        base = _u16(base)
+        if base.shape != (M, N):
+            raise ValueError("base shape mismatch")
+        bp = _ptr(base)
+    y = np.empty((M, N), dtype=np.float64)
+    lib().oracle_lora_expand(_ptr(l), _ptr(b), bp or None, _ptr(y), M, N, R, float(scale))
+    return y
 
 
 def combine_f32(partials) -> np.ndarray:

@@ -36,6 +36,12 @@
  *       reads key/value head h / (H / Hkv).  Scores, softmax and the weighted
  *       sum in fp64, unrounded; exp from libm.
  *
+ *   LoRA expand  y[m][n] = base[m][n] + scale * sum_r l[m][r] * b[n][r]
+ *       The other low-rank multiplication of a LoRA layer ("Reproducible LoRA
+ *       Inference Through Deterministic Split-K Reduction", abstract, speaks of
+ *       low-rank LoRA multiplications; the shrink output l feeds it).  fp64,
+ *       unrounded; base may be absent (then 0).
+ *
  *   Bit differences  popcount(a XOR b), and the count of differing elements.
  *       The check that "God Does Not Play Dice: Enforcing Batch Invariance in
  *       Agentic Kernel Generation" (abstract) asks for: bitwise consistency of
@@ -232,6 +238,22 @@ void oracle_decode_attention(const uint16_t *q, const uint16_t *k, const uint16_
         }
     }
     (void)threads;
+}
+
+/* --------------------------------------------------------- LoRA expand ---- */
+
+/* l [M][R] fp32, b [N][R] bf16, base [M][N] bf16 or NULL; y [M][N] fp64. */
+void oracle_lora_expand(const float *l, const uint16_t *b, const uint16_t *base, double *y,
+                        int64_t M, int64_t N, int64_t R, double scale)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t r = 0; r < R; ++r)
+                acc += (double)l[m * R + r] * bf16_value(b[n * R + r]);
+            y[m * N + n] = (base ? bf16_value(base[m * N + n]) : 0.0) + scale * acc;
+        }
+    }
 }
 
 /* ------------------------------------------------------- bit differences ---- */

@@ -35,7 +35,7 @@ class _Guarded:
 
     # position of the batch-size argument in each launching entry point
     M_ARG = {"bi_rmsnorm": 3, "bi_gemm": 3, "bi_gemm_with_config": 4, "bi_lora_shrink": 3,
-             "bi_gemm_splitk": 3, "bi_gemm_mswitch_control": 3, "bi_decode_attention": 5,
+             "bi_gemm_splitk": 3, "bi_gemm_mswitch_control": 3, "bi_decode_attention": 5, "bi_lora_expand": 4,
              "bi_lora_shrink_two_pass": 3, "bi_lora_shrink_atomic": 3, "bi_row_bitdiff": 6}
 
     def __init__(self, lib):
@@ -82,6 +82,7 @@ def _load():
     L.bi_decode_attention.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i, p, ctypes.c_size_t, p]
     L.bi_decode_attention_workspace_bytes.argtypes = [i64, i64, i64, i64, i]
     L.bi_decode_attention_workspace_bytes.restype = ctypes.c_size_t
+    L.bi_lora_expand.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i64, ctypes.c_float, p]
     L.bi_status_str.restype = ctypes.c_char_p
     return L
 
@@ -233,3 +234,14 @@ def test_decode_attention_validation(lib):
     assert f(X, W, Y, L, X + (1 << 26), *a, 256, WS, need - 1, None) == BI_ERR_WORKSPACE
     assert f(X, W, Y, L, X, *a, 256, WS, need, None) == BI_ERR_ALIAS
     assert f(None, None, None, None, None, 0, 32, 8, 128, 1000, 256, None, 0, None) == BI_OK
+
+
+def test_lora_expand_validation(lib):
+    f = lib.bi_lora_expand
+    assert f(X, None, None, Y, 4, 4096, 16, 16, 16, 0, 4096, 1.0, None) == BI_ERR_NULL
+    assert f(X, W, None, Y, 4, 4096, 8, 16, 16, 0, 4096, 1.0, None) == BI_ERR_UNSUPPORTED
+    assert f(X, W, None, Y, 4, 4100, 16, 16, 16, 0, 4100, 1.0, None) == BI_ERR_ALIGN
+    assert f(X, W, WS, Y, 4, 4096, 16, 16, 16, 4000, 4096, 1.0, None) == BI_ERR_SHAPE
+    assert f(X, W, Y + 16, Y, 4, 4096, 16, 16, 16, 4096, 4096, 1.0, None) == BI_ERR_ALIAS
+    assert f(X, W, None, X, 4, 4096, 16, 16, 16, 0, 4096, 1.0, None) == BI_ERR_ALIAS
+    assert f(None, W, None, None, 0, 4096, 16, 16, 16, 0, 4096, 1.0, None) == BI_OK

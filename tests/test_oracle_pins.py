@@ -521,3 +521,37 @@ def test_attention_dominant_key_and_masked_tail():
     assert np.all(np.isfinite(o))
     vd = oracle.bf16_decode(v)
     assert np.allclose(o[:, :, :], vd[:, 2, :, :], rtol=0, atol=1e-12 * 8)
+
+
+# ------------------------------------------------------------ LoRA expand --
+
+def test_lora_expand_integer_inputs_exact():
+    g = synth.rng(801)
+    l = g.integers(-50, 50, size=(7, 16)).astype(np.float32)
+    b = synth.int_bf16((13, 16), 802, -8, 8)
+    base = synth.int_bf16((7, 13), 803, -100, 100)
+    bi = oracle.bf16_decode(b).astype(np.int64)
+    exact = oracle.bf16_decode(base).astype(np.int64) + 3 * (l.astype(np.int64) @ bi.T)
+    assert np.array_equal(oracle.lora_expand(l, b, base, scale=3.0), exact.astype(np.float64))
+    assert np.array_equal(oracle.lora_expand(l, b, None, scale=1.0), (l.astype(np.int64) @ bi.T).astype(np.float64))
+
+
+def test_lora_expand_brute_force_rational():
+    g = synth.rng(804)
+    l = (g.standard_normal((3, 16)) * 3).astype(np.float32)
+    b = random_bf16_wide((5, 16), 805, binades=6)
+    base = random_bf16_wide((3, 5), 806, binades=4)
+    y = oracle.lora_expand(l, b, base, scale=0.5)
+    for m in range(3):
+        for n in range(5):
+            terms = [Fraction(float(l[m, r])) * bf16_fraction(int(b[n, r])) for r in range(16)]
+            exact = bf16_fraction(int(base[m, n])) + Fraction(1, 2) * sum(terms, Fraction(0))
+            bound = 16 * Fraction(1, 2 ** 52) * (abs(bf16_fraction(int(base[m, n]))) + sum(abs(t) for t in terms))
+            assert abs(Fraction(float(y[m, n])) - exact) <= bound
+
+
+def test_lora_expand_zero_scale_returns_base():
+    base = synth.normal_bf16((4, 9), 807)
+    l = np.ones((4, 16), np.float32)
+    b = synth.normal_bf16((9, 16), 808)
+    assert np.array_equal(oracle.lora_expand(l, b, base, scale=0.0), oracle.bf16_decode(base))
