@@ -15,7 +15,7 @@
 // workgroup owns.  The configuration is picked from (N, K) alone.
 //
 // Data path per workgroup (4 wavefronts, 2 x 2 over the tile):
-//   HBM/L2 --global_load_lds_dwordx4--> LDS (2 stages of BK = 64)
+//   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS (ring of 4 stages of BK = 32)
 //          --ds_read_b128--> VGPR fragments --MFMA--> fp32 accumulators
 //   epilogue: accumulators -> bf16 (round to nearest even) -> 8-byte stores.
 // LDS rows are 128 bytes (64 bf16 of one matrix row); their eight 16-byte
@@ -94,29 +94,36 @@ __device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int &
   tn = in_g / gsize;
 }
 
-// Per-lane source offsets (in elements, relative to the stage's k0) of the
-// direct-to-LDS loads of one operand tile.  Wavefront wv, instruction i fills
-// LDS rows [i*64 + wv*16, +16): lane l writes 16 bytes at row (l >> 2),
+// Direct-to-LDS loads of one operand tile through a buffer resource: each lane
+// keeps a constant 32-bit byte offset and the stage's k offset travels in the
+// scalar offset, so a stage costs no vector address arithmetic.  Wavefront
+// wv, instruction i fills LDS rows [i*64 + wv*16, +16): lane l writes 16 bytes
+// at row (l >> 2),
 // physical chunk (l & 3), which holds logical chunk (l & 3) ^ swz(row).
 // Rows past the matrix edge are clamped to its last row (loaded, never stored).
 template <int ROWS>
 struct LoadPlan {
   static constexpr int N = ROWS / 64;
-  int off[N];
-  __device__ __forceinline__ void init(int row0, int row_limit, int64_t ld, int wv, int lane) {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int off[N];  // byte offsets of this lane's 16-byte pieces, relative to the matrix base
+  __device__ __forceinline__ void init(const uint16_t *g, int rows_total, int row0, int row_limit,
+                                       int64_t ld, int K, int wv, int lane) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)g, (short)0,
+                                             (int)(((int64_t)(rows_total - 1) * ld + K) * 2),
+                                             0x00020000);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int r = i * 64 + wv * 16 + (lane >> 2);
       int gr = row0 + r;
       gr = gr < row_limit ? gr : row_limit - 1;
-      off[i] = (int)(gr * ld) + (((lane & 3) ^ swz(r)) << 3);
+      off[i] = ((int)(gr * ld) + (((lane & 3) ^ swz(r)) << 3)) * 2;
     }
   }
-  __device__ __forceinline__ void issue(char *lds, const uint16_t *__restrict__ g, int wv) const {
+  __device__ __forceinline__ void issue(char *lds, int k0, int wv) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       lds_void *dst = (lds_void *)(lds + (i * 64 + wv * 16) * kRowBytes);
-      __builtin_amdgcn_global_load_lds((const void *)(g + off[i]), dst, 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, off[i], k0 * 2, 0, 0);
     }
   }
 };
@@ -191,13 +198,13 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[BN / 64][BM / 64], c
                                               const uint16_t *__restrict__ x,
                                               const uint16_t *__restrict__ w, int M, int N,
                                               int nkb, int64_t ldx, int64_t ldw, int m0, int n0,
-                                              int wv, int lane) {
+                                              int wv, int lane, int kspan) {
   using C = Cfg<BN, BM>;
   const int wn = wv >> 1, wm = wv & 1;
   LoadPlan<BN> pw;
   LoadPlan<BM> px;
-  pw.init(n0, N, ldw, wv, lane);
-  px.init(m0, M, ldx, wv, lane);
+  pw.init(w, N, n0, N, ldw, kspan, wv, lane);
+  px.init(x, M, m0, M, ldx, kspan, wv, lane);
 
 #pragma unroll
   for (int i = 0; i < C::FN; ++i)
@@ -209,8 +216,8 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[BN / 64][BM / 64], c
   for (int s = 0; s < kStages; ++s) {
     if (s < nkb) {
       char *buf = lds + s * C::STAGE;
-      pw.issue(buf, w + s * BK, wv);
-      px.issue(buf + C::W_BYTES, x + s * BK, wv);
+      pw.issue(buf, s * BK, wv);
+      px.issue(buf + C::W_BYTES, s * BK, wv);
     }
   }
   wait_stages_after<C::LPS>(min(kStages - 1, nkb - 1));
@@ -234,8 +241,8 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[BN / 64][BM / 64], c
     wait_vmcnt<2 * C::LPS>();
     barrier_no_fence();
     __builtin_amdgcn_sched_barrier(0);
-    pw.issue(cur, w + (kb + kStages) * BK, wv);
-    px.issue(cur + C::W_BYTES, x + (kb + kStages) * BK, wv);
+    pw.issue(cur, (kb + kStages) * BK, wv);
+    px.issue(cur + C::W_BYTES, (kb + kStages) * BK, wv);
     read_frags<BN, BM>(f0, nxt, 0, wn, wm, lane);
     mfma_step<BN, BM>(acc, f1);
     interleave<C::FN * C::FM, C::LPS, C::FN + C::FM>();
@@ -277,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   const int n0 = tn * BN, m0 = tm * BM;
 
   f32x16 acc[C::FN][C::FM];
-  gemm_mainloop<BN, BM>(acc, lds, x, w, M, N, K / BK, ldx, ldw, m0, n0, wv, lane);
+  gemm_mainloop<BN, BM>(acc, lds, x, w, M, N, K / BK, ldx, ldw, m0, n0, wv, lane, K);
 
   // Epilogue.  Accumulator block (i, j) of this wavefront, register v, holds
   // n = base_n + 8*(v/4) + 4*(lane/32) + v%4 and m = base_m + lane%32: four
@@ -323,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_partial_kernel(
 
   f32x16 acc[C::FN][C::FM];
   gemm_mainloop<BN, BM>(acc, lds, x + (int64_t)s * kc, w + (int64_t)s * kc, M, N, kc / BK, ldx,
-                        ldw, m0, n0, wv, lane);
+                        ldw, m0, n0, wv, lane, kc);
 
   float *part = ws + (int64_t)s * M * N;
 #pragma unroll
