@@ -18,7 +18,7 @@
 //   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS (ring of 4 stages of BK = 32)
 //          --ds_read_b128--> VGPR fragments --MFMA--> fp32 accumulators
 //   epilogue: accumulators -> bf16 (round to nearest even) -> 8-byte stores.
-// LDS rows are 128 bytes (64 bf16 of one matrix row); their eight 16-byte
+// LDS rows are 64 bytes (32 bf16 of one matrix row); their four 16-byte
 // chunks are XOR-permuted by a function of the row so that the 32 rows a
 // fragment read touches spread over all LDS banks.  Rows beyond M (or N) are
 // loaded as copies of the last valid row and never stored, so no row's
@@ -40,8 +40,6 @@ constexpr int kStages = 4;             // LDS ring depth: 3 stages of loads in f
 // wavefronts reading concurrently, where the plain layout costs 2x.
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 template <int BN, int BM>
 struct Cfg {
   static constexpr int WN = BN / 2, WM = BM / 2;    // wavefront tile (n x m)
@@ -53,26 +51,6 @@ struct Cfg {
   static_assert(BN % 64 == 0 && BM % 64 == 0, "tile must split over 2x2 wavefronts");
   static_assert(3 * LPS < 64, "vmcnt range");
 };
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() {
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
-}
-// Workgroup barrier without the release/acquire fence of __syncthreads(): the
-// fence would also wait for every outstanding global->LDS load, which would
-// collapse the prefetch ring.  The waits each use needs are explicit; the
-// empty asm statements keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void barrier_no_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Map the launch index to a tile.  Workgroups are dispatched round-robin over
 // the 8 XCDs (index % 8); each XCD gets a contiguous range of logical tiles,

@@ -16,7 +16,7 @@
 //
 // Three ways to run it, all computing the same partials p_s:
 //   fused     (bi_lora_shrink): one kernel.  A workgroup is S wavefronts over
-//             one 16-row block; wavefront s computes p_s, the S partials meet in
+//             16-row blocks; wavefront s computes p_s, the S partials meet in
 //             LDS (the on-chip fp32 workspace) and wavefront 0 folds them in
 //             order.  No second launch, no atomics, no counters.
 //   two-pass  (bi_lora_shrink_two_pass): the split spans workgroups; partials go
@@ -26,7 +26,19 @@
 //             its partial into the zeroed output with a floating-point atomic,
 //             in arrival order.  The nondeterministic control.
 // The shrink reads x once from HBM (2*K bytes a row) and the small a from
-// cache, so it is bound by HBM bandwidth.
+// cache, so it is bound by HBM bandwidth.  Two things decide how close it gets:
+// how many requests a byte of x costs, and how often a is fetched again.
+//   staged kernel (S = 8, 16, the deterministic split): each wavefront keeps
+//     its chunk of a in registers for the whole launch; x reaches LDS through
+//     direct-to-LDS loads of whole 128-byte lines (1 KiB per instruction), two
+//     pieces in flight per wavefront, and is read back in the matrix-core
+//     layout.  Workgroups are persistent over row blocks, so a is fetched once
+//     per workgroup rather than once per row block.
+//   streamed kernel (other splits, and the two-pass partials): x and a go
+//     straight to registers in the matrix-core layout, a group of 8 steps per
+//     load batch, up to 3 batches in flight.
+// Every kernel feeds the matrix core the same operands in the same step
+// order, so they all produce the same bits.
 #include "common.h"
 
 namespace bi {
@@ -37,131 +49,107 @@ constexpr int kRowsPerWave = 16;
 constexpr int kRowsPerBlock = kRowsPerWave * (kThreads / 64);
 constexpr int kR = 16;        // LoRA rank handled by the 16x16x32 instruction
 constexpr int kStep = 32;     // k per matrix-core step
-constexpr int kGroup = 8;     // steps whose loads are issued together
 
 enum Mode { kStoreOut = 0, kStoreWs = 1, kAtomic = 2 };
 
-// One wavefront: 16 rows x 16 ranks over k in [k0, k0 + steps*32).
-// Operand roles: the A operand is the LoRA matrix (16 ranks x 32 k), the B
-// operand is x (32 k x 16 rows).  Lane l supplies rank / row (l & 15) and
-// k = step*32 + (l >> 4)*8 .. +7 of both operands, so products pair matching
-// k.  Output lane l holds row (l & 15), ranks 4*(l >> 4) .. +3.
-template <int MODE>
+// Operand roles of every kernel here: the A operand is the LoRA matrix
+// (16 ranks x 32 k), the B operand is x (32 k x 16 rows).  Lane l supplies
+// rank / row (l & 15) and k = step*32 + (l >> 4)*8 .. +7 of both operands, so
+// products pair matching k.  Output lane l holds row (l & 15), ranks
+// 4*(l >> 4) .. +3.
+__device__ __forceinline__ f32x4 mfma_step(bf16x8 a, bf16x8 x, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, x, acc, 0, 0, 0);
+}
+
+// Partial of one wavefront over STEPS steps (compile-time count): loads go out
+// in batches of G steps, DEPTH batches ahead of the math (64 registers a batch,
+// so DEPTH is capped by the wavefronts a workgroup puts on each SIMD).  xp / ap point at
+// this lane's first 16-byte piece of x and a.
+template <int STEPS, int MAXDEPTH>
+__device__ __forceinline__ f32x4 chunk_streamed(const bf16x8 *xp, const bf16x8 *ap) {
+  constexpr int G = STEPS < 8 ? STEPS : 8;
+  constexpr int NG = STEPS / G;
+  constexpr int DEPTH = NG < MAXDEPTH ? NG : MAXDEPTH;
+  static_assert(STEPS % G == 0, "step count");
+  bf16x8 xf[DEPTH][G], af[DEPTH][G];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < DEPTH; ++g) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      xf[g][i] = __builtin_nontemporal_load(xp + (g * G + i) * (kStep / 8));
+      af[g][i] = ap[(g * G + i) * (kStep / 8)];
+    }
+  }
+  // Keep the batch together: without this the scheduler trades loads in flight
+  // for registers.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) acc = mfma_step(af[g % DEPTH][i], xf[g % DEPTH][i], acc);
+    if (g + DEPTH < NG) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        xf[g % DEPTH][i] = __builtin_nontemporal_load(xp + ((g + DEPTH) * G + i) * (kStep / 8));
+        af[g % DEPTH][i] = ap[((g + DEPTH) * G + i) * (kStep / 8)];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return acc;
+}
+
+// Same partial for a step count known only at run time (shapes outside the
+// compiled set): one step at a time.
+__device__ __forceinline__ f32x4 chunk_plain(const bf16x8 *xp, const bf16x8 *ap, int steps) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < steps; ++t)
+    acc = mfma_step(ap[t * (kStep / 8)], __builtin_nontemporal_load(xp + t * (kStep / 8)), acc);
+  return acc;
+}
+
+template <int STEPS, int MAXDEPTH>
+__device__ __forceinline__ f32x4 chunk_partial(const bf16x8 *xp, const bf16x8 *ap, int steps) {
+  if constexpr (STEPS > 0) {
+    (void)steps;
+    return chunk_streamed<STEPS, MAXDEPTH>(xp, ap);
+  } else {
+    return chunk_plain(xp, ap, steps);
+  }
+}
+
+// Two-pass partials: grid (row blocks of 64, S); wavefront w of workgroup
+// (bx, s) computes p_s of rows bx*64 + w*16 .. +15.  STEPS = 0: run-time count.
+template <int STEPS, int MODE>
 __global__ __launch_bounds__(kThreads) void shrink_partial_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ a, float *__restrict__ out,
-    int M, int K, int64_t ldx, int64_t lda, int64_t ldo, int chunk) {
+    int M, int64_t ldx, int64_t lda, int64_t ldo, int chunk) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int mw = blockIdx.x * kRowsPerBlock + wv * kRowsPerWave;
   if (mw >= M) return;  // every row of this wavefront is past the batch
   const int s = blockIdx.y;
   const int k0 = s * chunk;
-  const int steps = chunk / kStep;
-
   int gm = mw + (lane & 15);
   gm = gm < M ? gm : M - 1;  // rows past M read a copy of the last row, never stored
   const int koff = (lane >> 4) * 8;
   const bf16x8 *xp = reinterpret_cast<const bf16x8 *>(x + (int64_t)gm * ldx + k0 + koff);
   const bf16x8 *ap = reinterpret_cast<const bf16x8 *>(a + (int64_t)(lane & 15) * lda + k0 + koff);
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  bf16x8 xf[kGroup], af[kGroup];
-  // Prefetch group 0, then keep one group of loads in flight ahead of the math.
-  const int ngroups = (steps + kGroup - 1) / kGroup;
-#pragma unroll
-  for (int i = 0; i < kGroup; ++i) {
-    if (i < steps) {
-      xf[i] = __builtin_nontemporal_load(xp + i * (kStep / 8));
-      af[i] = ap[i * (kStep / 8)];
-    }
-  }
-  for (int g = 0; g < ngroups; ++g) {
-    bf16x8 xn[kGroup], an[kGroup];
-    const int base = (g + 1) * kGroup;
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      if (base + i < steps) {
-        xn[i] = __builtin_nontemporal_load(xp + (base + i) * (kStep / 8));
-        an[i] = ap[(base + i) * (kStep / 8)];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      if (g * kGroup + i < steps) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], xf[i], acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      xf[i] = xn[i];
-      af[i] = an[i];
-    }
-  }
-
+  const f32x4 acc = chunk_partial<STEPS, 3>(xp, ap, chunk / kStep);
   const int m = mw + (lane & 15);
   if (m >= M) return;
   const int r0 = (lane >> 4) * 4;
-  if (MODE == kStoreOut) {
-    *reinterpret_cast<f32x4 *>(out + (int64_t)m * ldo + r0) = acc;
-  } else if (MODE == kStoreWs) {
-    *reinterpret_cast<f32x4 *>(out + ((int64_t)s * M + m) * kR + r0) = acc;
-  } else {
-    float *o = out + (int64_t)m * ldo + r0;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) unsafeAtomicAdd(o + v, acc[v]);
-  }
+  if (MODE == kStoreOut) *reinterpret_cast<f32x4 *>(out + (int64_t)m * ldo + r0) = acc;
+  else *reinterpret_cast<f32x4 *>(out + ((int64_t)s * M + m) * kR + r0) = acc;
 }
 
-// Fused split-K: blockDim = 64 * S; wavefront s computes p_s of the 16 rows
-// [blockIdx.x * 16, +16) over chunk s.  Same operand roles, k mapping and step
-// order as shrink_partial_kernel.  MODE: kStoreOut folds through LDS (and, if
-// ws != nullptr, also stores each p_s there); kAtomic adds each p_s into y.
+// Stores (or adds) the partial of wavefront s for rows m0 .. m0+15 and, in the
+// folding modes, the fold of the S partials through LDS (part holds S x 64
+// lanes; the caller places a barrier between the writes and wavefront 0's read).
 template <int S, int MODE>
-__global__ __launch_bounds__(64 * S) void shrink_fused_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ a, float *__restrict__ y,
-    float *__restrict__ ws, int M, int K, int64_t ldx, int64_t lda, int64_t ldy) {
-  const int lane = threadIdx.x & 63;
-  const int s = threadIdx.x >> 6;
-  const int m0 = blockIdx.x * kRowsPerWave;
-  const int chunk = K / S;
-  const int k0 = s * chunk;
-  const int steps = chunk / kStep;
-
-  int gm = m0 + (lane & 15);
-  gm = gm < M ? gm : M - 1;  // rows past M read a copy of the last row, never stored
-  const int koff = (lane >> 4) * 8;
-  const bf16x8 *xp = reinterpret_cast<const bf16x8 *>(x + (int64_t)gm * ldx + k0 + koff);
-  const bf16x8 *ap = reinterpret_cast<const bf16x8 *>(a + (int64_t)(lane & 15) * lda + k0 + koff);
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  bf16x8 xf[kGroup], af[kGroup];
-  const int ngroups = (steps + kGroup - 1) / kGroup;
-#pragma unroll
-  for (int i = 0; i < kGroup; ++i) {
-    if (i < steps) {
-      xf[i] = __builtin_nontemporal_load(xp + i * (kStep / 8));
-      af[i] = ap[i * (kStep / 8)];
-    }
-  }
-  for (int g = 0; g < ngroups; ++g) {
-    bf16x8 xn[kGroup], an[kGroup];
-    const int base = (g + 1) * kGroup;
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      if (base + i < steps) {
-        xn[i] = __builtin_nontemporal_load(xp + (base + i) * (kStep / 8));
-        an[i] = ap[(base + i) * (kStep / 8)];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      if (g * kGroup + i < steps) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], xf[i], acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      xf[i] = xn[i];
-      af[i] = an[i];
-    }
-  }
-
+__device__ __forceinline__ void emit(f32x4 acc, f32x4 (*part)[64], float *y, float *ws, int M,
+                                     int64_t ldy, int m0, int s, int lane) {
   const int m = m0 + (lane & 15);
   const int r0 = (lane >> 4) * 4;
   if (MODE == kAtomic) {
@@ -177,9 +165,9 @@ __global__ __launch_bounds__(64 * S) void shrink_fused_kernel(
     return;
   }
   if (ws != nullptr && m < M) *reinterpret_cast<f32x4 *>(ws + ((int64_t)s * M + m) * kR + r0) = acc;
-  __shared__ f32x4 part[S][64];
   part[s][lane] = acc;
-  __syncthreads();
+  wait_lgkmcnt0();
+  barrier_no_fence();
   if (s == 0 && m < M) {
     f32x4 t = part[0][lane];
 #pragma unroll
@@ -188,15 +176,141 @@ __global__ __launch_bounds__(64 * S) void shrink_fused_kernel(
   }
 }
 
-template <int MODE>
-void launch_fused(int S, dim3 grid, hipStream_t st, const uint16_t *x, const uint16_t *a, float *y,
-                  float *ws, int M, int K, int64_t ldx, int64_t lda, int64_t ldy) {
-  switch (S) {
-    case 1: hipLaunchKernelGGL((shrink_fused_kernel<1, MODE>), grid, dim3(64), 0, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
-    case 2: hipLaunchKernelGGL((shrink_fused_kernel<2, MODE>), grid, dim3(128), 0, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
-    case 4: hipLaunchKernelGGL((shrink_fused_kernel<4, MODE>), grid, dim3(256), 0, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
-    case 8: hipLaunchKernelGGL((shrink_fused_kernel<8, MODE>), grid, dim3(512), 0, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
-    default: hipLaunchKernelGGL((shrink_fused_kernel<16, MODE>), grid, dim3(1024), 0, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
+// Streamed fused kernel: blockDim = 64 * S; wavefront s computes p_s of the 16
+// rows [blockIdx.x * 16, +16) over chunk s.  STEPS = 0: run-time count.
+template <int S, int STEPS, int MODE>
+__global__ __launch_bounds__(64 * S) void shrink_fused_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ a, float *__restrict__ y,
+    float *__restrict__ ws, int M, int K, int64_t ldx, int64_t lda, int64_t ldy) {
+  const int lane = threadIdx.x & 63;
+  const int s = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * kRowsPerWave;
+  const int chunk = K / S;
+  const int k0 = s * chunk;
+  int gm = m0 + (lane & 15);
+  gm = gm < M ? gm : M - 1;  // rows past M read a copy of the last row, never stored
+  const int koff = (lane >> 4) * 8;
+  const bf16x8 *xp = reinterpret_cast<const bf16x8 *>(x + (int64_t)gm * ldx + k0 + koff);
+  const bf16x8 *ap = reinterpret_cast<const bf16x8 *>(a + (int64_t)(lane & 15) * lda + k0 + koff);
+  const f32x4 acc = chunk_partial<STEPS, (S >= 16 ? 1 : 3)>(xp, ap, chunk / kStep);
+  __shared__ f32x4 part[S][64];
+  emit<S, MODE>(acc, part, y, ws, M, ldy, m0, s, lane);
+}
+
+// Staged fused kernel, S = 8 or 16 wavefronts, STEPS steps per chunk.
+//
+// A piece is 16 rows x PS steps of one wavefront's chunk (PS * 64 bytes a
+// row); each wavefront owns a ring of two pieces in LDS.  One direct-to-LDS
+// instruction moves 1 KiB = 16/PS whole row segments; lane l of instruction i
+// loads row i*(16/PS) + l/U (U = PS*4 sixteen-byte units a row), unit
+// (l % U) ^ row, so unit u of row r sits at position u ^ r: a matrix-core read
+// (16 rows, one unit each, per 16 lanes) then touches 16 different 16-byte
+// bank groups.  The LDS of a workgroup is S*16 KiB of pieces plus two S x 1 KiB
+// fold buffers (144 KiB for S = 8, 160 KiB for S = 16): one workgroup per CU.  The pieces of a wavefront run block after block over the
+// workgroup's row blocks (blockIdx.x, + gridDim.x, ...); while one is read, the
+// next is in flight.
+template <int S, int STEPS, int MODE>
+__global__ __launch_bounds__(64 * S, 1) void shrink_staged_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ a, float *__restrict__ y,
+    float *__restrict__ ws, int M, int K, int64_t ldx, int64_t lda, int64_t ldy, int nblocks) {
+  constexpr int PS = 64 / S;                 // steps per piece: 8 (S = 8) or 4 (S = 16)
+  constexpr int NP = STEPS / PS;             // pieces per row block
+  constexpr int ROWB = PS * 64;              // bytes of one row in a piece
+  constexpr int U = ROWB / 16;               // 16-byte units of one row in a piece
+  constexpr int RPI = 1024 / ROWB;           // rows per load instruction
+  constexpr int NI = 16 / RPI;               // load instructions per piece (= PS)
+  constexpr int PIECE = 16 * ROWB;
+  static_assert(S * PS == 64 && STEPS % PS == 0 && U >= 16 && NP % 2 == 0, "staged shape");
+  // The two slots are separate LDS objects: the compiler's wait counting can
+  // then tell that a read of one slot does not depend on a load into the other.
+  __shared__ __attribute__((aligned(1024))) char xs0[S][PIECE];
+  __shared__ __attribute__((aligned(1024))) char xs1[S][PIECE];
+  __shared__ f32x4 part[2][S][64];
+
+  const int lane = threadIdx.x & 63;
+  const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int k0 = s * STEPS * kStep;
+
+  const int nmine = (nblocks - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int npieces = nmine * NP;
+  const int64_t xbytes = (int64_t)M * ldx * 2;
+
+  // Piece j of this wavefront -> LDS slot j & 1.
+  auto issue = [&](int j) {
+    const int m0 = ((int)blockIdx.x + (j / NP) * (int)gridDim.x) * kRowsPerWave;
+    const int kp = k0 + (j % NP) * PS * kStep;
+    const uint16_t *base = x + (int64_t)m0 * ldx;
+    const int64_t left = xbytes - (int64_t)m0 * ldx * 2;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)base, (short)0, (int)(left < 0x7FFFFFFF ? left : 0x7FFFFFFF), 0x00020000);
+    char *slot = (j & 1) ? xs1[s] : xs0[s];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = i * RPI + lane / U;
+      const int gr = (m0 + row < M ? m0 + row : M - 1) - m0;  // rows past M: copy of the last
+      const int off = (int)((gr * ldx + kp + (((lane % U) ^ row) * 8)) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(slot + i * 1024), 16, off, 0, 0, 0);
+    }
+  };
+
+  // x first: its loads go to HBM and take longest; the chunk of a (cache
+  // hits after the first workgroups) follows, in the matrix-core layout, kept
+  // in registers for the whole launch.
+  issue(0);
+  if (npieces > 1) issue(1);
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 af[STEPS];
+  {
+    const bf16x8 *ap =
+        reinterpret_cast<const bf16x8 *>(a + (int64_t)(lane & 15) * lda + k0 + (lane >> 4) * 8);
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) af[t] = ap[t * (kStep / 8)];
+  }
+  // Matrix-core steps over piece j (slot j & 1) into acc.
+  const int r = lane & 15;
+  auto compute = [&](int j, int p, f32x4 &acc) {
+    const char *slot = (j & 1) ? xs1[s] : xs0[s];
+    bf16x8 xv[PS];
+#pragma unroll
+    for (int t = 0; t < PS; ++t) {
+      const int u = t * 4 + (lane >> 4);
+      xv[t] = *reinterpret_cast<const bf16x8 *>(slot + r * ROWB + ((u ^ r) << 4));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all reads of the piece in flight together
+#pragma unroll
+    for (int t = 0; t < PS; ++t) acc = mfma_step(af[p * PS + t], xv[t], acc);
+    wait_lgkmcnt0();  // the slot's reads are done before it is refilled
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Every block but the last: each piece has a successor in flight and the
+  // piece two ahead exists, so the loop body has no branches (the compiler's
+  // wait counting then sees straight-line code).
+  int bi = 0;
+  for (; bi + 1 < nmine; ++bi) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int j = bi * NP + p;
+      wait_vmcnt<NI>();
+      compute(j, p, acc);
+      issue(j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int m0 = ((int)blockIdx.x + bi * (int)gridDim.x) * kRowsPerWave;
+    emit<S, MODE>(acc, part[bi & 1], y, ws, M, ldy, m0, s, lane);
+  }
+  {  // last block: pieces npieces - NP .. npieces - 1, nothing more to issue
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int j = bi * NP + p;
+      if (p + 1 < NP) wait_vmcnt<NI>();
+      else wait_vmcnt<0>();
+      compute(j, p, acc);
+    }
+    const int m0 = ((int)blockIdx.x + bi * (int)gridDim.x) * kRowsPerWave;
+    emit<S, MODE>(acc, part[bi & 1], y, ws, M, ldy, m0, s, lane);
   }
 }
 
@@ -254,6 +368,88 @@ dim3 partial_grid(int64_t M, int S) {
   return dim3((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)S);
 }
 
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// Calls f(IntC<steps>) for the compiled step counts, f(IntC<0>) (run-time
+// count) otherwise.
+template <typename F>
+void with_steps(int steps, F &&f) {
+  switch (steps) {
+    case 8: f(IntC<8>{}); break;
+    case 16: f(IntC<16>{}); break;
+    case 32: f(IntC<32>{}); break;
+    case 64: f(IntC<64>{}); break;
+    case 128: f(IntC<128>{}); break;
+    default: f(IntC<0>{}); break;
+  }
+}
+
+template <int S, int STEPS, int MODE>
+void launch_streamed(dim3 grid, hipStream_t st, const uint16_t *x, const uint16_t *a, float *y,
+                     float *ws, int64_t M, int64_t K, int64_t ldx, int64_t lda, int64_t ldy) {
+  hipLaunchKernelGGL((shrink_fused_kernel<S, STEPS, MODE>), grid, dim3(64 * S), 0, st, x, a, y, ws,
+                     (int)M, (int)K, ldx, lda, ldy);
+}
+
+template <int S, int STEPS, int MODE>
+void launch_staged(int grid, int nblocks, hipStream_t st, const uint16_t *x, const uint16_t *a,
+                   float *y, float *ws, int64_t M, int64_t K, int64_t ldx, int64_t lda,
+                   int64_t ldy) {
+  hipLaunchKernelGGL((shrink_staged_kernel<S, STEPS, MODE>), dim3(grid), dim3(64 * S), 0, st, x,
+                     a, y, ws, (int)M, (int)K, ldx, lda, ldy, nblocks);
+}
+
+// One fused launch: the staged kernel for the deterministic splits (S = 8, 16)
+// at 8 or 16 steps a chunk, the streamed kernel otherwise.
+template <int MODE>
+void launch_fused(int S, hipStream_t st, const uint16_t *x, const uint16_t *a, float *y, float *ws,
+                  int64_t M, int64_t K, int64_t ldx, int64_t lda, int64_t ldy) {
+  const int steps = (int)(K / S / kStep);
+  const int64_t nblocks = (M + kRowsPerWave - 1) / kRowsPerWave;
+  // the staged loads address x with 32-bit byte offsets inside a 16-row block
+  if (((S == 8 && steps == 16) || (S == 16 && (steps == 8 || steps == 16))) &&
+      ldx < (int64_t(1) << 26)) {
+    const int grid = (int)(nblocks < cu_count() ? nblocks : cu_count());
+    if (S == 8) launch_staged<8, 16, MODE>(grid, (int)nblocks, st, x, a, y, ws, M, K, ldx, lda, ldy);
+    else if (steps == 16) launch_staged<16, 16, MODE>(grid, (int)nblocks, st, x, a, y, ws, M, K, ldx, lda, ldy);
+    else launch_staged<16, 8, MODE>(grid, (int)nblocks, st, x, a, y, ws, M, K, ldx, lda, ldy);
+    return;
+  }
+  const dim3 grid((unsigned)nblocks);
+  with_steps(steps, [&](auto c) {
+    constexpr int ST = decltype(c)::value;
+    switch (S) {
+      case 1: launch_streamed<1, ST, MODE>(grid, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
+      case 2: launch_streamed<2, ST, MODE>(grid, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
+      case 4: launch_streamed<4, ST, MODE>(grid, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
+      case 8: launch_streamed<8, ST, MODE>(grid, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
+      default: launch_streamed<16, ST, MODE>(grid, st, x, a, y, ws, M, K, ldx, lda, ldy); break;
+    }
+  });
+}
+
+template <int MODE>
+void launch_partial(int S, hipStream_t st, const uint16_t *x, const uint16_t *a, float *out,
+                    int64_t M, int64_t K, int64_t ldx, int64_t lda, int64_t ldo) {
+  const int chunk = (int)(K / S);
+  with_steps(chunk / kStep, [&](auto c) {
+    constexpr int ST = decltype(c)::value;
+    hipLaunchKernelGGL((shrink_partial_kernel<ST, MODE>), partial_grid(M, S), dim3(kThreads), 0, st,
+                       x, a, out, (int)M, ldx, lda, ldo, chunk);
+  });
+}
+
 }  // namespace
 }  // namespace bi
 
@@ -273,9 +469,8 @@ extern "C" int bi_lora_shrink(const uint16_t *x, const uint16_t *a, float *y, in
   if (split_k > 1 && ws != nullptr && (st = validate_ws(x, a, y, M, K, R, ldx, lda, ldy, split_k, ws, ws_bytes)) != BI_OK)
     return st;
   if (M == 0) return BI_OK;
-  launch_fused<kStoreOut>(split_k, dim3((unsigned)((M + kRowsPerWave - 1) / kRowsPerWave)),
-                          (hipStream_t)stream, x, a, y, split_k > 1 ? static_cast<float *>(ws) : nullptr,
-                          (int)M, (int)K, ldx, lda, ldy);
+  launch_fused<kStoreOut>(split_k, (hipStream_t)stream, x, a, y,
+                          split_k > 1 ? static_cast<float *>(ws) : nullptr, M, K, ldx, lda, ldy);
   return launch_status();
 }
 
@@ -290,15 +485,12 @@ extern "C" int bi_lora_shrink_two_pass(const uint16_t *x, const uint16_t *a, flo
   }
   if (M == 0) return BI_OK;
   hipStream_t s = (hipStream_t)stream;
-  const int chunk = (int)(K / split_k);
   if (split_k == 1) {
-    hipLaunchKernelGGL(shrink_partial_kernel<kStoreOut>, partial_grid(M, 1), dim3(kThreads), 0, s,
-                       x, a, y, (int)M, (int)K, ldx, lda, ldy, chunk);
+    launch_partial<kStoreOut>(1, s, x, a, y, M, K, ldx, lda, ldy);
     return launch_status();
   }
   float *wsf = static_cast<float *>(ws);
-  hipLaunchKernelGGL(shrink_partial_kernel<kStoreWs>, partial_grid(M, split_k), dim3(kThreads), 0,
-                     s, x, a, wsf, (int)M, (int)K, ldx, lda, (int64_t)kR, chunk);
+  launch_partial<kStoreWs>(split_k, s, x, a, wsf, M, K, ldx, lda, (int64_t)kR);
   if ((st = launch_status()) != BI_OK) return st;
   const int64_t n = M * kR;
   hipLaunchKernelGGL(shrink_combine_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
@@ -316,7 +508,6 @@ extern "C" int bi_lora_shrink_atomic(const uint16_t *x, const uint16_t *a, float
   hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, s, y, (int)M, ldy);
   if ((st = launch_status()) != BI_OK) return st;
-  launch_fused<kAtomic>(split_k, dim3((unsigned)((M + kRowsPerWave - 1) / kRowsPerWave)), s, x, a, y,
-                        nullptr, (int)M, (int)K, ldx, lda, ldy);
+  launch_fused<kAtomic>(split_k, s, x, a, y, nullptr, M, K, ldx, lda, ldy);
   return launch_status();
 }
