@@ -19,10 +19,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // tie into a round-up only when the kept part is odd), then truncate.  NaN is
 // returned as a quiet NaN with its sign.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x0040u;
+  // a select, not a branch: the conversion sits in the stores of every kernel
+  return (uint16_t)((u & 0x7FFFFFFFu) > 0x7F800000u ? quiet : rounded);
 }
 
 // bf16 bit pattern -> fp32 (exact).
