@@ -246,17 +246,33 @@ def cpu_baseline(x, g, ws_h, a, eps):
 
 
 def _time_loop(torch, fn, n, reps=7):
-    """Median over reps of (n launches) / n, in ms, with HIP events."""
+    """Median over reps of (n launches) / n, in ms.  The n launches are
+    captured once in a HIP graph and the graph is replayed between HIP events,
+    so the figure is device time, not the host's launch rate (the kernels here
+    issue no memset, which keeps them safe to capture)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        for i in range(n):
-            fn(i)
+        g.replay()
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1) / n)
+    del g
     ts.sort()
     return ts[len(ts) // 2]
 
@@ -277,10 +293,16 @@ def sweep(path, bi, torch, dev, to_dev):
     for si, (K, N) in enumerate(workloads.LLAMA8B["shapes"]):
         W = to_dev(workloads.llama8b_w(si))
         xpool = to_dev(workloads.llama8b_x(K))
-        for M in (1, 16, 128, 512, 1024, 2048, 4096, 8192):
+        # below M ~ 1000 the weight read dominates: rotate weight copies past the cache
+        cw = copies(2 * N * K)
+        Ws = [W] + [W.clone() for _ in range(cw - 1)]
+        for M in (1, 5, 33, 127, 512, 1000, 2048, 4096, 8192):
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            n = 20 if M >= 2048 else 50
-            ms = _time_loop(torch, lambda i: bi.bi_gemm(xpool[:M], W, y=y), n)
+            n = 20 if M >= 2048 else 4 * cw
+            if M >= 2048:
+                ms = _time_loop(torch, lambda i: bi.bi_gemm(xpool[:M], W, y=y), n)
+            else:
+                ms = _time_loop(torch, lambda i: bi.bi_gemm(xpool[:M], Ws[i % cw], y=y), n)
             fl = 2.0 * M * N * K
             by = 2.0 * (M * K + N * K + M * N)
             t_roof = max(fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
@@ -295,8 +317,8 @@ def sweep(path, bi, torch, dev, to_dev):
                 S = bi.bi_gemm_splitk_for(N, K)
                 ws = torch.empty(bi.bi_gemm_splitk_workspace_bytes(M, N, S), dtype=torch.uint8,
                                  device=dev)
-                ms2 = _time_loop(torch, lambda i: bi.bi_gemm_splitk(xpool[:M], W, y=y, split_k=S,
-                                                                     ws=ws), n)
+                ms2 = _time_loop(torch, lambda i: bi.bi_gemm_splitk(xpool[:M], Ws[i % cw], y=y,
+                                                                     split_k=S, ws=ws), n)
                 recs.append({"kernel": "bi_gemm_splitk", "K": K, "N": N, "M": M, "split_k": S,
                              "us": ms2 * 1e3, "tflops": fl / (ms2 * 1e-3) / 1e12,
                              "gbs": by / (ms2 * 1e-3) / 1e9,
@@ -304,7 +326,7 @@ def sweep(path, bi, torch, dev, to_dev):
                 print(f"# sweep gemm_splitk K={K} N={N} M={M} S={S}: {ms2*1e3:.1f} us "
                       f"({recs[-1]['gbs']:.0f} GB/s) vs bi_gemm {ms*1e3:.1f} us",
                       file=sys.stderr, flush=True)
-        del W, xpool
+        del W, Ws, xpool
     # RMSNorm over M (K = 4096), rotating buffers
     K = 4096
     wv = to_dev(synth.normal_bf16((K,), 2002, mean=1.0, std=0.1))
@@ -346,6 +368,46 @@ def sweep(path, bi, torch, dev, to_dev):
               f"atomic {res['atomic8']*1e3:.1f}us "
               f"unsplit {res['unsplit']*1e3:.1f}us", file=sys.stderr, flush=True)
         del xs
+    # Decode attention (Llama-3-8B heads: H = 32, Hkv = 8, D = 128; split 256),
+    # every sequence at T tokens; bytes = the K and V caches read once.
+    H, Hkv, D, T = 32, 8, 128, 4096
+    for B in (1, 8, 32, 64):
+        per = 2 * B * T * Hkv * D * 2
+        c = copies(per)
+        ks = [torch.randn((B, T, Hkv, D), device=dev).to(torch.bfloat16) for _ in range(c)]
+        vs = [torch.randn((B, T, Hkv, D), device=dev).to(torch.bfloat16) for _ in range(c)]
+        q = torch.randn((B, H, D), device=dev).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+        ws = torch.empty(bi.bi_decode_attention_workspace_bytes(B, H, T, D, 256), dtype=torch.uint8,
+                         device=dev)
+        ms = _time_loop(torch, lambda i: bi.bi_decode_attention(q, ks[i % c], vs[i % c], lens, o=o,
+                                                                 split_size=256, ws=ws), 4 * c)
+        by = float(per + 2 * 2 * B * H * D)
+        recs.append({"kernel": "bi_decode_attention", "B": B, "T": T, "H": H, "Hkv": Hkv, "D": D,
+                     "us": ms * 1e3, "gbs": by / (ms * 1e-3) / 1e9,
+                     "frac_hbm": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "rotating_copies": c})
+        print(f"# sweep attention B={B} T={T}: {ms*1e3:.1f} us {recs[-1]['gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        del ks, vs
+    # LoRA expand y = bf16(base + l . b^T) at d_model = 4096, rank 16
+    N, R = 4096, 16
+    b = torch.randn((N, R), device=dev).to(torch.bfloat16)
+    for M in (512, 4096, 16384):
+        per = 4 * M * N
+        c = copies(per)
+        ls = [torch.randn((M, R), device=dev) for _ in range(c)]
+        bases = [torch.randn((M, N), device=dev).to(torch.bfloat16) for _ in range(c)]
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(c)]
+        ms = _time_loop(torch, lambda i: bi.bi_lora_expand(ls[i % c], b, base=bases[i % c],
+                                                            y=ys[i % c]), 4 * c)
+        by = 4.0 * M * N + 4 * M * R + 2 * N * R
+        recs.append({"kernel": "bi_lora_expand", "M": M, "N": N, "R": R, "us": ms * 1e3,
+                     "gbs": by / (ms * 1e-3) / 1e9, "frac_hbm": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "rotating_copies": c})
+        print(f"# sweep expand M={M}: {ms*1e3:.1f} us {recs[-1]['gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        del ls, bases, ys
     with open(path, "w") as f:
         for r in recs:
             f.write(json.dumps(r) + "\n")
