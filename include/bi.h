@@ -260,10 +260,12 @@ int bi_lora_shrink_atomic(const uint16_t *x, const uint16_t *a, float *y,
  *   deployment, never derived from the batch.
  *   ws, ws_bytes: fp32 workspace of bi_decode_attention_workspace_bytes(B, H,
  *   Tmax, D, split_size) bytes (per-chunk max, sum and weighted values).
- * Order of every output: per chunk of split_size tokens, scores with d
- * ascending, max, exp, a sum in a fixed lane/xor order, values with t
- * ascending; chunks folded with c ascending (see attention.hip).  The result
- * for sequence b depends on its own q, cache and length only.
+ * Order of every output: per chunk of split_size tokens, each score summed
+ * over fixed lane slices of d and a fixed xor tree; max, exp and a sum in a
+ * fixed lane/xor order; values summed per lane over a fixed token subset,
+ * then a fixed xor tree and the four wavefronts in order; chunks folded with c
+ * ascending (see attention.hip).  The result for sequence b depends on its own
+ * q, cache and length only.
  */
 int bi_decode_attention(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
                         const int32_t *lens, uint16_t *o,

@@ -12,17 +12,26 @@
 // of C tokens (C fixed by the caller, never by the batch); the number of
 // chunks follows the sequence's own length T_b only.
 //
+// Decode attention streams the whole cache, so it is bound by HBM bandwidth:
+// 2 * T_b * Hkv * D * 2 bytes of K and V per sequence.  Reads are coalesced:
+// a token's row of D bf16 is read by L = D/8 consecutive lanes, 16 bytes
+// each, so one wavefront instruction covers 64/L whole token rows.
+//
 // Order of every output o[b][h][:] (G = H / Hkv query heads share key/value
-// head h / G):
-//   chunk c, token t:  s_t = (sum_{d ascending} q[d] * k_t[d]) * scale   (fp32)
+// head h / G; workgroup = 4 wavefronts; wavefront w owns tokens
+// [w*C/4, (w+1)*C/4) of the chunk; lane l owns d = 8*(l % L) .. +7 and the
+// tokens t = w*C/4 + i*(64/L) + l/L, i ascending):
+//   score s_t = (sum over the L lanes of token t, xor butterfly L/2 .. 1, of
+//               the lane's 8 products summed in ascending d) * scale   (fp32)
 //   chunk c:  m_c = max_t s_t;  p_t = exp(s_t - m_c);
 //             l_c = sum_t p_t over lanes j = t mod 64 (t ascending within a
 //             lane), then a fixed xor tree over the 64 lanes;
-//             a_c[d] = sum_{t ascending} p_t * v_t[d]
+//             a_c[d] = per lane sum of p_t * v_t[d] over its tokens (i
+//             ascending), then the lanes of one d combined by the xor
+//             butterfly over the token-lane offsets, then the four
+//             wavefronts as ((w0 + w1) + w2) + w3
 //   combine:  M = max_c m_c;  L = sum_{c ascending} exp(m_c - M) * l_c;
 //             O[d] = sum_{c ascending} exp(m_c - M) * a_c[d];  o = bf16(O / L).
-// Decode attention streams the whole cache, so it is bound by HBM bandwidth:
-// 2 * T_b * Hkv * D * 2 bytes of K and V per sequence.
 #include "common.h"
 
 namespace bi {
@@ -31,12 +40,17 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxG = 8;
 constexpr int kMaxC = 512;
+constexpr int kBatch = 8;  // token rows loaded per wavefront before use
 
-template <int D>
+// D: head size; GM: a power of two >= G (register arrays are sized by it);
+// C: the split size.
+template <int D, int GM, int C>
 __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ lens, float *__restrict__ ws,
-    int H, int Hkv, int Tmax, int C, int nc_max, float scale) {
+    int H, int Hkv, int Tmax, int nc_max, float scale) {
+  constexpr int L = D / 8;      // lanes per token row
+  constexpr int TPI = 64 / L;   // token rows per wavefront instruction
   const int c = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int G = H / Hkv;
   int T = lens[b];
@@ -45,46 +59,69 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
   if (t0 >= T) return;  // this sequence has fewer chunks (uniform over the block)
   const int n = min(C, T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int dl = lane % L, tl = lane / L;
+  constexpr int tpw = C / 4;  // tokens per wavefront
+  constexpr int nbatch = tpw / (TPI * kBatch) > 0 ? tpw / (TPI * kBatch) : 1;
+  constexpr int per_batch = tpw / (TPI * nbatch);  // instructions per batch (<= kBatch)
+  static_assert(per_batch <= kBatch && per_batch * nbatch * TPI == tpw, "chunk split");
 
-  __shared__ float qs[kMaxG][D];
   __shared__ float ps[kMaxG][kMaxC];
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int g = i / D, d = i % D;
-    qs[g][d] = bf16_to_f32(q[((int64_t)b * H + kh * G + g) * D + d]);
-  }
-  __syncthreads();
+  __shared__ float red[4][GM][D];
 
-  // Scores: thread tid owns tokens tid, tid + 256, ... of the chunk.
+  // This lane's slice of every query head, fp32.
+  float qf[GM][8];
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    const int gg = g < G ? g : 0;
+    const u32x4 qv = *reinterpret_cast<const u32x4 *>(q + ((int64_t)b * H + kh * G + gg) * D + dl * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qf[g][2 * j] = lo_bf16(qv[j]);
+      qf[g][2 * j + 1] = hi_bf16(qv[j]);
+    }
+  }
+
   const int64_t row_stride = (int64_t)Hkv * D;  // elements between tokens
-  const uint16_t *kbase = kc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D;
-  for (int t = tid; t < C; t += kThreads) {
-    float s[kMaxG];
+  const uint16_t *kbase = kc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D + dl * 8;
+  const uint16_t *vbase = vc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D + dl * 8;
+  const int tw = wv * tpw + tl;  // this lane's first token in the chunk
+
+  // Loads of batch bt of the chunk.  Tokens at or past n load token n - 1
+  // instead (in bounds and finite; their weight is exactly 0 below), so the
+  // loads are unconditional; nothing past the sequence's length is read.
+  auto load_batch = [&](u32x4 *dst, const uint16_t *base, int bt) {
 #pragma unroll
-    for (int g = 0; g < kMaxG; ++g) s[g] = 0.0f;
-    if (t < n) {
-      const u32x4 *kr = reinterpret_cast<const u32x4 *>(kbase + (int64_t)t * row_stride);
-      u32x4 kv[D / 8];
+    for (int i = 0; i < per_batch; ++i) {
+      const int t = min(tw + (bt * per_batch + i) * TPI, n - 1);
+      dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + (int64_t)t * row_stride));
+    }
+  };
+  // Scores (batches one at a time, to keep registers for occupancy).
+#pragma unroll 1
+  for (int bt = 0; bt < nbatch; ++bt) {
+    u32x4 kv[per_batch];
+    load_batch(kv, kbase, bt);
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) kv[i] = __builtin_nontemporal_load(kr + i);
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
+    for (int i = 0; i < per_batch; ++i) {
+      {
+        const int t = tw + (bt * per_batch + i) * TPI;
+        float kf[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float k0 = lo_bf16(kv[i][j]), k1 = hi_bf16(kv[i][j]);
-          const int d = i * 8 + j * 2;
+          kf[2 * j] = lo_bf16(kv[i][j]);
+          kf[2 * j + 1] = hi_bf16(kv[i][j]);
+        }
 #pragma unroll
-          for (int g = 0; g < kMaxG; ++g) {
-            if (g < G) {
-              s[g] = s[g] + qs[g][d] * k0;
-              s[g] = s[g] + qs[g][d + 1] * k1;
-            }
-          }
+        for (int g = 0; g < GM; ++g) {
+          float part = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part = part + qf[g][e] * kf[e];
+#pragma unroll
+          for (int off = L / 2; off >= 1; off >>= 1) part = part + __shfl_xor(part, off, 64);
+          if (g < G && dl == 0) ps[g][t] = t < n ? part * scale : -INFINITY;
         }
       }
     }
-#pragma unroll
-    for (int g = 0; g < kMaxG; ++g)
-      if (g < G) ps[g][t] = t < n ? s[g] * scale : -INFINITY;
   }
   __syncthreads();
 
@@ -111,13 +148,52 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
   }
   __syncthreads();
 
-  // Weighted values: pair (g, d) -> sum over tokens in ascending order.
-  const uint16_t *vbase = vc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D;
+  // Weighted values.
+  float acc[GM][8];
+#pragma unroll
+  for (int g = 0; g < GM; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
+#pragma unroll 1
+  for (int bt = 0; bt < nbatch; ++bt) {
+    u32x4 vv[per_batch];
+    load_batch(vv, vbase, bt);
+#pragma unroll
+    for (int i = 0; i < per_batch; ++i) {
+      // p_t = exp(-inf) = 0 for t >= n, whose row is a copy of token n - 1
+      const int t = tw + (bt * per_batch + i) * TPI;
+      float vf[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vf[2 * j] = lo_bf16(vv[i][j]);
+        vf[2 * j + 1] = hi_bf16(vv[i][j]);
+      }
+#pragma unroll
+      for (int g = 0; g < GM; ++g) {
+        const float p = g < G ? ps[g][t] : 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = acc[g][e] + p * vf[e];
+      }
+    }
+  }
+  // Lanes of one d slice (same dl, different tl) combine by xor over the
+  // token-lane offsets, then wavefront partials meet in LDS.
+#pragma unroll
+  for (int g = 0; g < GM; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int off = L; off < 64; off <<= 1) acc[g][e] = acc[g][e] + __shfl_xor(acc[g][e], off, 64);
+  if (tl == 0) {
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wv][g][dl * 8 + e] = acc[g][e];
+  }
+  __syncthreads();
   for (int pi = tid; pi < G * D; pi += kThreads) {
     const int g = pi / D, d = pi % D;
-    float a = 0.0f;
-#pragma unroll 8
-    for (int t = 0; t < n; ++t) a = a + ps[g][t] * bf16_to_f32(vbase[(int64_t)t * row_stride + d]);
+    const float a = ((red[0][g][d] + red[1][g][d]) + red[2][g][d]) + red[3][g][d];
     wsb[(int64_t)g * nc_max * (D + 2) + d] = a;
   }
 }
@@ -144,6 +220,11 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float *__restrict
 }
 
 int64_t nchunks(int64_t Tmax, int C) { return (Tmax + C - 1) / C; }
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 
 }  // namespace
 }  // namespace bi
@@ -185,16 +266,28 @@ extern "C" int bi_decode_attention(const uint16_t *q, const uint16_t *k_cache,
   hipStream_t s = (hipStream_t)stream;
   float *wsf = static_cast<float *>(ws);
   const dim3 g1((unsigned)nc, (unsigned)Hkv, (unsigned)B), g2((unsigned)H, (unsigned)B);
-  if (D == 64) {
-    hipLaunchKernelGGL(attn_chunk_kernel<64>, g1, dim3(kThreads), 0, s, q, k_cache, v_cache, lens,
-                       wsf, (int)H, (int)Hkv, (int)Tmax, split_size, nc, scale);
-    hipLaunchKernelGGL(attn_combine_kernel<64>, g2, dim3(64), 0, s, wsf, lens, o, (int)H,
+  const int G = (int)(H / Hkv);
+  auto chunk = [&](auto dc, auto gc) {
+    constexpr int DD = decltype(dc)::value, GG = decltype(gc)::value;
+    if (split_size == 128)
+      hipLaunchKernelGGL((attn_chunk_kernel<DD, GG, 128>), g1, dim3(kThreads), 0, s, q, k_cache,
+                         v_cache, lens, wsf, (int)H, (int)Hkv, (int)Tmax, nc, scale);
+    else if (split_size == 256)
+      hipLaunchKernelGGL((attn_chunk_kernel<DD, GG, 256>), g1, dim3(kThreads), 0, s, q, k_cache,
+                         v_cache, lens, wsf, (int)H, (int)Hkv, (int)Tmax, nc, scale);
+    else
+      hipLaunchKernelGGL((attn_chunk_kernel<DD, GG, 512>), g1, dim3(kThreads), 0, s, q, k_cache,
+                         v_cache, lens, wsf, (int)H, (int)Hkv, (int)Tmax, nc, scale);
+    hipLaunchKernelGGL(attn_combine_kernel<DD>, g2, dim3(DD), 0, s, wsf, lens, o, (int)H,
                        (int)Tmax, split_size, nc);
-  } else {
-    hipLaunchKernelGGL(attn_chunk_kernel<128>, g1, dim3(kThreads), 0, s, q, k_cache, v_cache, lens,
-                       wsf, (int)H, (int)Hkv, (int)Tmax, split_size, nc, scale);
-    hipLaunchKernelGGL(attn_combine_kernel<128>, g2, dim3(128), 0, s, wsf, lens, o, (int)H,
-                       (int)Tmax, split_size, nc);
-  }
+  };
+  auto by_g = [&](auto dc) {
+    if (G == 1) chunk(dc, IntC<1>{});
+    else if (G == 2) chunk(dc, IntC<2>{});
+    else if (G <= 4) chunk(dc, IntC<4>{});
+    else chunk(dc, IntC<8>{});
+  };
+  if (D == 64) by_g(IntC<64>{});
+  else by_g(IntC<128>{});
   return launch_status();
 }
