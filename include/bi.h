@@ -289,9 +289,11 @@ size_t bi_decode_attention_workspace_bytes(int64_t B, int64_t H, int64_t Tmax, i
  *   base  [M, N] bf16, row stride ldbase, or NULL (then 0); may equal y when
  *         ldbase == ldy (in-place add)
  *   y     [M, N] bf16, row stride ldy
- *   R == 16; N >= 8, N % 8 == 0, N <= 2^23; ldy, ldbase % 8 == 0.
- * Order of every output: products summed in ascending r in fp32, the sum
- * multiplied by scale, added to base in fp32, rounded to nearest even once.
+ *   R == 16; N >= 8, N % 8 == 0, N <= 2^23; ldy, ldbase, ldb % 8 == 0;
+ *   y, base and b 16-byte aligned, l 4-byte aligned (else BI_ERR_ALIGN).
+ * Order of every output: acc = fma(l[m][r], b[n][r], acc) in fp32 for r
+ * ascending from acc = 0, then base + scale * acc in fp32, rounded to nearest
+ * even once.
  */
 int bi_lora_expand(const float *l, const uint16_t *b, const uint16_t *base, uint16_t *y,
                    int64_t M, int64_t N, int64_t R,

@@ -4,14 +4,16 @@
 // abstract: LoRA adds low-rank multiplications to a layer; the fp32 shrink
 // output l (rank R) is expanded back to the layer width and added to the base
 // output.  With R = 16 the reduction is short, so there is no split: every
-// output sums its 16 products in ascending r in fp32, scales, adds the base
-// and rounds to bf16 once -- the same order at any batch size.
+// output accumulates its 16 products in ascending r with fp32 fused
+// multiply-adds (one rounding per step), scales, adds the base and rounds to
+// bf16 once -- the same order at any batch size.
 //
 // The expand streams base and y (4 bytes an output) and is bound by HBM
-// bandwidth; the 16 multiply-adds per output run on the vector ALUs.  A
-// 256-thread workgroup owns a 64 x 128 output tile: it stages the tile's 128
-// rows of b and 64 rows of l in LDS once, and each thread computes 4 rows x 8
-// consecutive columns with 16-byte loads and stores of base and y.
+// bandwidth.  Each wavefront owns 512 consecutive columns -- 8 per lane,
+// 16 bytes of base and of y -- for a run of rows: its lanes hold their 8
+// columns of b in registers for the whole run, each row's 16 values
+// of l arrive through the scalar cache, and the row loop keeps kAhead rows of
+// base loads in flight.
 #include "common.h"
 
 namespace bi {
@@ -19,51 +21,73 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kR = 16;
-constexpr int TM = 64, TN = 128;
+constexpr int kCols = 512;   // columns per wavefront: 64 lanes x 8
+constexpr int kAhead = 8;    // rows of base loads in flight per wavefront
 
+// grid: x = column slice of 512, y = row group; wavefront w of the workgroup
+// takes rows [(blockIdx.y * 4 + w) * rpw, + rpw).  HAS_BASE: base != NULL.
+template <bool HAS_BASE>
 __global__ __launch_bounds__(kThreads) void lora_expand_kernel(
     const float *__restrict__ l, const uint16_t *__restrict__ b, const uint16_t *base,
     uint16_t *y, int M, int N, int64_t ldl, int64_t ldb, int64_t ldbase, int64_t ldy,
-    float scale) {
-  const int m0 = blockIdx.x * TM, n0 = blockIdx.y * TN;
-  __shared__ float bs[TN][kR + 1];  // +1: rows land in different banks
-  __shared__ float ls[TM][kR + 1];
-  for (int i = threadIdx.x; i < TN * kR; i += kThreads) {
-    const int r = i % kR, n = i / kR;
-    const int gn = n0 + n < N ? n0 + n : N - 1;
-    bs[n][r] = bf16_to_f32(b[(int64_t)gn * ldb + r]);
-  }
-  for (int i = threadIdx.x; i < TM * kR; i += kThreads) {
-    const int r = i % kR, m = i / kR;
-    const int gm = m0 + m < M ? m0 + m : M - 1;
-    ls[m][r] = l[(int64_t)gm * ldl + r];
-  }
-  __syncthreads();
+    float scale, int rpw) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * kCols + lane * 8;
+  const bool col_ok = n0 < N;  // N is a multiple of 8: a lane's 8 columns are all in or all out
+  const int nn = col_ok ? n0 : N - 8;
+  const int m_begin = (blockIdx.y * 4 + wv) * rpw;
+  if (m_begin >= M) return;
+  const int m_end = min(M, m_begin + rpw);
 
-  const int tc = threadIdx.x & 15, tr = threadIdx.x >> 4;
-  const int nn = n0 + tc * 8;
-  if (nn >= N) return;
+  // This lane's 8 columns of b, as loaded (bf16 pairs): column j, ranks
+  // 2i, 2i+1 in word i of bw[j].  Kept packed to leave registers for loads in
+  // flight; each value is widened where it is used (exact).
+  u32x4 bw[8][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int mm = tr * 4 + i;
-    const int m = m0 + mm;
-    if (m >= M) break;
-    u32x4 bv = {0u, 0u, 0u, 0u};
-    if (base) bv = *reinterpret_cast<const u32x4 *>(base + (int64_t)m * ldbase + nn);
+  for (int j = 0; j < 8; ++j) {
+    const u32x4 *br = reinterpret_cast<const u32x4 *>(b + (int64_t)(nn + j) * ldb);
+    bw[j][0] = br[0];
+    bw[j][1] = br[1];
+  }
+  auto bval = [&](int j, int r) -> float {
+    const uint32_t w = bw[j][r >> 3][(r >> 1) & 3];
+    return (r & 1) ? hi_bf16(w) : lo_bf16(w);
+  };
+
+  auto row = [&](int m, u32x4 bv) {
+    const float *lr = l + (int64_t)m * ldl;  // uniform over the wavefront: scalar loads
+    float lv[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) lv[r] = lr[r];
     u32x4 o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int k = 0; k < 4; ++k) {
       float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
-        acc0 = acc0 + ls[mm][r] * bs[tc * 8 + 2 * j][r];
-        acc1 = acc1 + ls[mm][r] * bs[tc * 8 + 2 * j + 1][r];
+        acc0 = __builtin_fmaf(lv[r], bval(2 * k, r), acc0);
+        acc1 = __builtin_fmaf(lv[r], bval(2 * k + 1, r), acc1);
       }
-      const float v0 = lo_bf16(bv[j]) + scale * acc0;
-      const float v1 = hi_bf16(bv[j]) + scale * acc1;
-      o[j] = pack_bf16x2(v0, v1);
+      const float v0 = lo_bf16(bv[k]) + scale * acc0;
+      const float v1 = hi_bf16(bv[k]) + scale * acc1;
+      o[k] = pack_bf16x2(v0, v1);
     }
-    *reinterpret_cast<u32x4 *>(y + (int64_t)m * ldy + nn) = o;
+    if (col_ok) *reinterpret_cast<u32x4 *>(y + (int64_t)m * ldy + nn) = o;
+  };
+  auto load_base = [&](int m) -> u32x4 {
+    if (!HAS_BASE) return u32x4{0u, 0u, 0u, 0u};
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + (int64_t)m * ldbase + nn));
+  };
+
+  // Rows in batches of kAhead: all loads of a batch are issued before its math.
+  for (int m = m_begin; m < m_end; m += kAhead) {
+    u32x4 bv[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) bv[i] = load_base(min(m + i, m_end - 1));
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i)
+      if (m + i < m_end) row(m + i, bv[i]);
   }
 }
 
@@ -80,8 +104,8 @@ extern "C" int bi_lora_expand(const float *l, const uint16_t *b, const uint16_t 
   if (M < 0 || N < 8 || M > (1 << 30) || N > (1 << 23) || ldl < R || ldb < R || ldy < N ||
       (base && ldbase < N))
     return BI_ERR_SHAPE;
-  if ((N | ldy) & 7 || (base && (ldbase & 7)) || !aligned16(y) || (base && !aligned16(base)) ||
-      ((uintptr_t)l & 3) || ((uintptr_t)b & 1))
+  if ((N | ldy | ldb) & 7 || (base && (ldbase & 7)) || !aligned16(y) || (base && !aligned16(base)) ||
+      ((uintptr_t)l & 3) || !aligned16(b))
     return BI_ERR_ALIGN;
   const Span sy = span_of(y, M, N, ldy, 2);
   const bool in_place = base == y && ldbase == ldy;
@@ -89,8 +113,18 @@ extern "C" int bi_lora_expand(const float *l, const uint16_t *b, const uint16_t 
       (base && !in_place && overlap(sy, span_of(base, M, N, ldbase, 2))))
     return BI_ERR_ALIAS;
   if (M == 0) return BI_OK;
-  const dim3 grid((unsigned)((M + TM - 1) / TM), (unsigned)((N + TN - 1) / TN));
-  hipLaunchKernelGGL(lora_expand_kernel, grid, dim3(kThreads), 0, (hipStream_t)stream, l, b, base,
-                     y, (int)M, (int)N, ldl, ldb, ldbase, ldy, scale);
+  // Rows per wavefront: enough wavefronts to fill the chip (about 2048), at
+  // least kAhead rows each so the b registers are amortised.
+  const int64_t slices = (N + kCols - 1) / kCols;
+  int64_t rpw = (M * slices + 2047) / 2048;
+  rpw = rpw < kAhead ? kAhead : ((rpw + kAhead - 1) / kAhead) * kAhead;
+  const int64_t groups = (M + 4 * rpw - 1) / (4 * rpw);
+  const dim3 grid((unsigned)slices, (unsigned)groups);
+  if (base)
+    hipLaunchKernelGGL(lora_expand_kernel<true>, grid, dim3(kThreads), 0, (hipStream_t)stream, l, b,
+                       base, y, (int)M, (int)N, ldl, ldb, ldbase, ldy, scale, (int)rpw);
+  else
+    hipLaunchKernelGGL(lora_expand_kernel<false>, grid, dim3(kThreads), 0, (hipStream_t)stream, l, b,
+                       base, y, (int)M, (int)N, ldl, ldb, ldbase, ldy, scale, (int)rpw);
   return launch_status();
 }

@@ -241,6 +241,8 @@ def test_lora_expand_validation(lib):
     assert f(X, None, None, Y, 4, 4096, 16, 16, 16, 0, 4096, 1.0, None) == BI_ERR_NULL
     assert f(X, W, None, Y, 4, 4096, 8, 16, 16, 0, 4096, 1.0, None) == BI_ERR_UNSUPPORTED
     assert f(X, W, None, Y, 4, 4100, 16, 16, 16, 0, 4100, 1.0, None) == BI_ERR_ALIGN
+    assert f(X, W + 2, None, Y, 4, 4096, 16, 16, 16, 0, 4096, 1.0, None) == BI_ERR_ALIGN  # b
+    assert f(X, W, None, Y, 4, 4096, 16, 16, 20, 0, 4096, 1.0, None) == BI_ERR_ALIGN     # ldb
     assert f(X, W, WS, Y, 4, 4096, 16, 16, 16, 4000, 4096, 1.0, None) == BI_ERR_SHAPE
     assert f(X, W, Y + 16, Y, 4, 4096, 16, 16, 16, 4096, 4096, 1.0, None) == BI_ERR_ALIAS
     assert f(X, W, None, X, 4, 4096, 16, 16, 16, 0, 4096, 1.0, None) == BI_ERR_ALIAS
