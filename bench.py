@@ -327,10 +327,23 @@ def sweep(path, bi, torch, dev, to_dev):
                       f"({recs[-1]['gbs']:.0f} GB/s) vs bi_gemm {ms*1e3:.1f} us",
                       file=sys.stderr, flush=True)
         del W, Ws, xpool
+    # Reference: a plain device copy (torch) of the same bytes as RMSNorm at
+    # M = 2048 / 8192 and of 512 MiB -- the practical read+write rate of HBM
+    # on this part, beside the 8 TB/s spec.
+    for nbytes in (16 << 20, 64 << 20, 512 << 20):
+        c = copies(2 * nbytes)
+        srcs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(c)]
+        dsts = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(c)]
+        ms = _time_loop(torch, lambda i: dsts[i % c].copy_(srcs[i % c]), 4 * c)
+        recs.append({"kernel": "device_copy_reference", "bytes_each_way": nbytes, "us": ms * 1e3,
+                     "gbs": 2.0 * nbytes / (ms * 1e-3) / 1e9,
+                     "frac_hbm": 2.0 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "rotating_copies": c})
+        print(f"# sweep copy {nbytes >> 20} MiB: {recs[-1]['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+        del srcs, dsts
     # RMSNorm over M (K = 4096), rotating buffers
     K = 4096
     wv = to_dev(synth.normal_bf16((K,), 2002, mean=1.0, std=0.1))
-    for M in (1, 7, 128, 2048, 8192):
+    for M in (1, 7, 128, 2048, 8192, 65536):
         per = 4 * M * K
         c = copies(per)
         xs = [torch.randn((M, K), device=dev).to(torch.bfloat16) for _ in range(c)]
@@ -344,7 +357,7 @@ def sweep(path, bi, torch, dev, to_dev):
         del xs, ys
     # LoRA shrink over M, three variants, rotating buffers
     a = to_dev(workloads.lora_inputs(1)[1])
-    for M in (1, 8, 64, 512, 4096):
+    for M in (1, 8, 64, 512, 4096, 16384, 65536):
         per = 2 * M * 4096
         c = copies(per)
         xs = [torch.randn((M, 4096), device=dev).to(torch.bfloat16) for _ in range(c)]
