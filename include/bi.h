@@ -260,8 +260,8 @@ int bi_lora_shrink_atomic(const uint16_t *x, const uint16_t *a, float *y,
  *   deployment, never derived from the batch.
  *   ws, ws_bytes: fp32 workspace of bi_decode_attention_workspace_bytes(B, H,
  *   Tmax, D, split_size) bytes (per-chunk max, sum and weighted values).
- * Order of every output: per chunk of split_size tokens, each score summed
- * over fixed lane slices of d and a fixed xor tree; max, exp and a sum in a
+ * Order of every output: per chunk of split_size tokens, each score a
+ * matrix-core dot product over d blocks of 32 in ascending order; max, exp and a sum in a
  * fixed lane/xor order; values summed per lane over a fixed token subset,
  * then a fixed xor tree and the four wavefronts in order; chunks folded with c
  * ascending (see attention.hip).  The result for sequence b depends on its own

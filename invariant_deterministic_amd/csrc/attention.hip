@@ -14,15 +14,15 @@
 //
 // Decode attention streams the whole cache, so it is bound by HBM bandwidth:
 // 2 * T_b * Hkv * D * 2 bytes of K and V per sequence.  Reads are coalesced:
-// a token's row of D bf16 is read by L = D/8 consecutive lanes, 16 bytes
-// each, so one wavefront instruction covers 64/L whole token rows.
+// keys in 64-byte pieces of 16 tokens per instruction (the matrix-core
+// layout), values as whole rows, D/8 lanes per token.
 //
 // Order of every output o[b][h][:] (G = H / Hkv query heads share key/value
 // head h / G; workgroup = 4 wavefronts; wavefront w owns tokens
 // [w*C/4, (w+1)*C/4) of the chunk; lane l owns d = 8*(l % L) .. +7 and the
 // tokens t = w*C/4 + i*(64/L) + l/L, i ascending):
-//   score s_t = (sum over the L lanes of token t, xor butterfly L/2 .. 1, of
-//               the lane's 8 products summed in ascending d) * scale   (fp32)
+//   score s_t = (q . k_t by v_mfma_f32_16x16x32_bf16 over d blocks of 32,
+//               ascending, fp32 accumulator) * scale
 //   chunk c:  m_c = max_t s_t;  p_t = exp(s_t - m_c);
 //             l_c = sum_t p_t over lanes j = t mod 64 (t ascending within a
 //             lane), then a fixed xor tree over the 64 lanes;
@@ -68,58 +68,53 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
   __shared__ float ps[kMaxG][kMaxC];
   __shared__ float red[4][GM][D];
 
-  // This lane's slice of every query head, fp32.
-  float qf[GM][8];
+  const int64_t row_stride = (int64_t)Hkv * D;  // elements between tokens
+  const uint16_t *vbase = vc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D + dl * 8;
+  const int tw = wv * tpw + tl;  // this lane's first token in the chunk (values)
+
+  // Scores on the matrix core: s = q . k as v_mfma_f32_16x16x32_bf16 over d
+  // blocks of 32 (ascending), query heads as the A rows (zero past G), 16
+  // tokens as the B columns.  Lane l supplies head / token (l & 15) and
+  // d = 32j + 8(l >> 4) .. +7 of block j; it receives s for token (l & 15),
+  // heads 4(l >> 4) .. +3.  A token's 64-byte piece of block j is read by 4
+  // lanes, so one load instruction covers 16 tokens.
+  constexpr int NJ = D / 32;
+  constexpr int NGRP = tpw / 16;                      // 16-token groups per wavefront
+  constexpr int GB = NGRP < 4 ? NGRP : 4;             // groups per load batch
+  bf16x8 qa[NJ];
+  {
+    const int g = lane & 15;
+    const uint16_t *qr = q + ((int64_t)b * H + kh * G + (g < G ? g : 0)) * D + (lane >> 4) * 8;
 #pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    const int gg = g < G ? g : 0;
-    const u32x4 qv = *reinterpret_cast<const u32x4 *>(q + ((int64_t)b * H + kh * G + gg) * D + dl * 8);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      qf[g][2 * j] = lo_bf16(qv[j]);
-      qf[g][2 * j + 1] = hi_bf16(qv[j]);
+    for (int j = 0; j < NJ; ++j) {
+      qa[j] = *reinterpret_cast<const bf16x8 *>(qr + 32 * j);
+      if (g >= G) qa[j] = bf16x8{};
     }
   }
-
-  const int64_t row_stride = (int64_t)Hkv * D;  // elements between tokens
-  const uint16_t *kbase = kc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D + dl * 8;
-  const uint16_t *vbase = vc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D + dl * 8;
-  const int tw = wv * tpw + tl;  // this lane's first token in the chunk
-
-  // Loads of batch bt of the chunk.  Tokens at or past n load token n - 1
-  // instead (in bounds and finite; their weight is exactly 0 below), so the
-  // loads are unconditional; nothing past the sequence's length is read.
-  auto load_batch = [&](u32x4 *dst, const uint16_t *base, int bt) {
-#pragma unroll
-    for (int i = 0; i < per_batch; ++i) {
-      const int t = min(tw + (bt * per_batch + i) * TPI, n - 1);
-      dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + (int64_t)t * row_stride));
-    }
-  };
-  // Scores (batches one at a time, to keep registers for occupancy).
+  const uint16_t *kb2 = kc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D + (lane >> 4) * 8;
+  const int tok = lane & 15;
 #pragma unroll 1
-  for (int bt = 0; bt < nbatch; ++bt) {
-    u32x4 kv[per_batch];
-    load_batch(kv, kbase, bt);
+  for (int gb = 0; gb < NGRP; gb += GB) {
+    // Tokens at or past n load token n - 1 (in bounds, finite; masked below).
+    bf16x8 kf[GB][NJ];
 #pragma unroll
-    for (int i = 0; i < per_batch; ++i) {
-      {
-        const int t = tw + (bt * per_batch + i) * TPI;
-        float kf[8];
+    for (int i = 0; i < GB; ++i) {
+      const int t = min(wv * tpw + (gb + i) * 16 + tok, n - 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          kf[2 * j] = lo_bf16(kv[i][j]);
-          kf[2 * j + 1] = hi_bf16(kv[i][j]);
-        }
+      for (int j = 0; j < NJ; ++j)
+        kf[i][j] = __builtin_nontemporal_load(
+            reinterpret_cast<const bf16x8 *>(kb2 + (int64_t)t * row_stride + 32 * j));
+    }
 #pragma unroll
-        for (int g = 0; g < GM; ++g) {
-          float part = 0.0f;
+    for (int i = 0; i < GB; ++i) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) part = part + qf[g][e] * kf[e];
+      for (int j = 0; j < NJ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], kf[i][j], acc, 0, 0, 0);
+      const int t = wv * tpw + (gb + i) * 16 + tok;
 #pragma unroll
-          for (int off = L / 2; off >= 1; off >>= 1) part = part + __shfl_xor(part, off, 64);
-          if (g < G && dl == 0) ps[g][t] = t < n ? part * scale : -INFINITY;
-        }
+      for (int v = 0; v < 4; ++v) {
+        const int g = 4 * (lane >> 4) + v;
+        if (g < G) ps[g][t] = t < n ? acc[v] * scale : -INFINITY;
       }
     }
   }
@@ -148,6 +143,16 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
   }
   __syncthreads();
 
+  // Value rows of batch bt.  Tokens at or past n load token n - 1 instead
+  // (in bounds and finite; their weight is exactly 0), so the loads are
+  // unconditional and nothing past the sequence's length is read.
+  auto load_batch = [&](u32x4 *dst, const uint16_t *base, int bt) {
+#pragma unroll
+    for (int i = 0; i < per_batch; ++i) {
+      const int t = min(tw + (bt * per_batch + i) * TPI, n - 1);
+      dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + (int64_t)t * row_stride));
+    }
+  };
   // Weighted values.
   float acc[GM][8];
 #pragma unroll
