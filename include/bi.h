@@ -257,14 +257,15 @@ int bi_lora_shrink_atomic(const uint16_t *x, const uint16_t *a, float *y,
  *   o        [B, H, D] bf16 output.
  *   D in {64, 128}; H % Hkv == 0 and H / Hkv <= 8 (grouped-query heads);
  *   split_size (tokens per chunk) in {128, 256, 512}: a constant of the
- *   deployment, never derived from the batch.
+ *   deployment, never derived from the batch.  split_size * Hkv * D * 2 must
+ *   stay below 2^31 (BI_ERR_UNSUPPORTED otherwise).
  *   ws, ws_bytes: fp32 workspace of bi_decode_attention_workspace_bytes(B, H,
  *   Tmax, D, split_size) bytes (per-chunk max, sum and weighted values).
  * Order of every output: per chunk of split_size tokens, each score a
  * matrix-core dot product over d blocks of 32 in ascending order; max, exp and a sum in a
- * fixed lane/xor order; values summed per lane over a fixed token subset,
- * then a fixed xor tree and the four wavefronts in order; chunks folded with c
- * ascending (see attention.hip).  The result for sequence b depends on its own
+ * fixed lane/xor order; the weights rounded to bf16 and the weighted values
+ * summed by matrix-core products over 32-token blocks in ascending order;
+ * chunks folded with c ascending (see attention.hip).  The result for sequence b depends on its own
  * q, cache and length only.
  */
 int bi_decode_attention(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,

@@ -15,21 +15,19 @@
 // Decode attention streams the whole cache, so it is bound by HBM bandwidth:
 // 2 * T_b * Hkv * D * 2 bytes of K and V per sequence.  Reads are coalesced:
 // keys in 64-byte pieces of 16 tokens per instruction (the matrix-core
-// layout), values as whole rows, D/8 lanes per token.
+// layout), values as whole rows straight into LDS, loaded while the scores
+// are computed.
 //
 // Order of every output o[b][h][:] (G = H / Hkv query heads share key/value
-// head h / G; workgroup = 4 wavefronts; wavefront w owns tokens
-// [w*C/4, (w+1)*C/4) of the chunk; lane l owns d = 8*(l % L) .. +7 and the
-// tokens t = w*C/4 + i*(64/L) + l/L, i ascending):
+// head h / G; workgroup = 4 wavefronts):
 //   score s_t = (q . k_t by v_mfma_f32_16x16x32_bf16 over d blocks of 32,
 //               ascending, fp32 accumulator) * scale
 //   chunk c:  m_c = max_t s_t;  p_t = exp(s_t - m_c);
 //             l_c = sum_t p_t over lanes j = t mod 64 (t ascending within a
 //             lane), then a fixed xor tree over the 64 lanes;
-//             a_c[d] = per lane sum of p_t * v_t[d] over its tokens (i
-//             ascending), then the lanes of one d combined by the xor
-//             butterfly over the token-lane offsets, then the four
-//             wavefronts as ((w0 + w1) + w2) + w3
+//             a_c[d] = sum over 32-token blocks, ascending, of matrix-core
+//             products bf16(p_t) * v_t[d] (v_mfma_f32_16x16x32_bf16, fp32
+//             accumulator)
 //   combine:  M = max_c m_c;  L = sum_{c ascending} exp(m_c - M) * l_c;
 //             O[d] = sum_{c ascending} exp(m_c - M) * a_c[d];  o = bf16(O / L).
 #include "common.h"
@@ -39,18 +37,28 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxG = 8;
-constexpr int kMaxC = 512;
-constexpr int kBatch = 8;  // token rows loaded per wavefront before use
 
-// D: head size; GM: a power of two >= G (register arrays are sized by it);
-// C: the split size.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// D: head size; GM: a power of two >= G; C: the split size.
 template <int D, int GM, int C>
 __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ lens, float *__restrict__ ws,
     int H, int Hkv, int Tmax, int nc_max, float scale) {
-  constexpr int L = D / 8;      // lanes per token row
-  constexpr int TPI = 64 / L;   // token rows per wavefront instruction
+  constexpr int NJ = D / 32;                                   // 32-wide d blocks (scores)
+  constexpr int VS = C * D * 2 <= 65536 ? C : 65536 / (D * 2);  // value rows per LDS pass
+  constexpr int NPASS = C / VS;
+  constexpr int RPI = 1024 / (D * 2);                          // value rows per load instruction
+  constexpr int LPR = 64 / RPI;                                // lanes per value row
+  constexpr int VI = VS / (RPI * 4);                           // load instructions per wavefront per pass
+  constexpr int tpw = C / 4;                                   // score tokens per wavefront
+  constexpr int NGRP = tpw / 16;
+  constexpr int GB = NGRP < 4 ? NGRP : 4;                      // 16-token groups per load batch
+  constexpr int CB = D / 64;                                   // 16-wide d blocks per wavefront (values)
+  static_assert(VS % 32 == 0 && VS * NPASS == C && VI >= 1 && CB >= 1 && NGRP % GB == 0, "shape");
+
   const int c = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
   const int G = H / Hkv;
   int T = lens[b];
@@ -58,19 +66,29 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
   const int t0 = c * C;
   if (t0 >= T) return;  // this sequence has fewer chunks (uniform over the block)
   const int n = min(C, T - t0);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int dl = lane % L, tl = lane / L;
-  constexpr int tpw = C / 4;  // tokens per wavefront
-  constexpr int nbatch = tpw / (TPI * kBatch) > 0 ? tpw / (TPI * kBatch) : 1;
-  constexpr int per_batch = tpw / (TPI * nbatch);  // instructions per batch (<= kBatch)
-  static_assert(per_batch <= kBatch && per_batch * nbatch * TPI == tpw, "chunk split");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  __shared__ float ps[kMaxG][kMaxC];
-  __shared__ float red[4][GM][D];
+  __shared__ __attribute__((aligned(1024))) uint16_t vs[VS * D];
+  __shared__ __attribute__((aligned(16))) float ps[GM][C];
 
   const int64_t row_stride = (int64_t)Hkv * D;  // elements between tokens
-  const uint16_t *vbase = vc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D + dl * 8;
-  const int tw = wv * tpw + tl;  // this lane's first token in the chunk (values)
+  const uint16_t *kseq = kc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D;
+  const uint16_t *vseq = vc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D;
+
+  // Value rows of pass `pass` -> vs (row-major, D per row), direct to LDS.
+  // Rows at or past n load row n - 1 (in bounds, finite; their weight is 0).
+  auto issue_v = [&](int pass) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)vseq, (short)0, (int)(((int64_t)(n - 1) * row_stride + D) * 2), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int row0 = (i * 4 + wv) * RPI;
+      const int t = min(pass * VS + row0 + lane / LPR, n - 1);
+      const int off = (int)(((int64_t)t * row_stride + (lane % LPR) * 8) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(vs + row0 * D), 16, off, 0, 0, 0);
+    }
+  };
 
   // Scores on the matrix core: s = q . k as v_mfma_f32_16x16x32_bf16 over d
   // blocks of 32 (ascending), query heads as the A rows (zero past G), 16
@@ -78,9 +96,6 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
   // d = 32j + 8(l >> 4) .. +7 of block j; it receives s for token (l & 15),
   // heads 4(l >> 4) .. +3.  A token's 64-byte piece of block j is read by 4
   // lanes, so one load instruction covers 16 tokens.
-  constexpr int NJ = D / 32;
-  constexpr int NGRP = tpw / 16;                      // 16-token groups per wavefront
-  constexpr int GB = NGRP < 4 ? NGRP : 4;             // groups per load batch
   bf16x8 qa[NJ];
   {
     const int g = lane & 15;
@@ -91,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
       if (g >= G) qa[j] = bf16x8{};
     }
   }
-  const uint16_t *kb2 = kc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D + (lane >> 4) * 8;
+  const uint16_t *kb2 = kseq + (lane >> 4) * 8;
   const int tok = lane & 15;
 #pragma unroll 1
   for (int gb = 0; gb < NGRP; gb += GB) {
@@ -105,6 +120,8 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
         kf[i][j] = __builtin_nontemporal_load(
             reinterpret_cast<const bf16x8 *>(kb2 + (int64_t)t * row_stride + 32 * j));
     }
+    // The first pass of values loads while the scores are computed.
+    if (gb == 0) issue_v(0);
 #pragma unroll
     for (int i = 0; i < GB; ++i) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -118,7 +135,9 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
       }
     }
   }
-  __syncthreads();
+  // The value loads may still be in flight: wait for the score stores only.
+  wait_lgkmcnt0();
+  barrier_no_fence();
 
   // Softmax pieces: wavefront w handles heads w, w + 4.
   float *wsb = ws + (((int64_t)b * H + kh * G) * nc_max + c) * (D + 2);
@@ -141,65 +160,65 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
       o[D + 1] = l;
     }
   }
-  __syncthreads();
 
-  // Value rows of batch bt.  Tokens at or past n load token n - 1 instead
-  // (in bounds and finite; their weight is exactly 0), so the loads are
-  // unconditional and nothing past the sequence's length is read.
-  auto load_batch = [&](u32x4 *dst, const uint16_t *base, int bt) {
+  // Weighted values on the matrix core: O[g][d] += P[g][t] V[t][d] as
+  // v_mfma_f32_16x16x32_bf16 over 32-token blocks, ascending, with P rounded
+  // to bf16 (nearest even).  Wavefront w owns d columns [64w, 64w + 64) in
+  // blocks of 16.  A operand: lane l supplies head (l & 15), tokens
+  // 8(l >> 4) .. +7 of the block; B operand: the same tokens of column
+  // (l & 15), read from the row-major LDS copy by two transposing reads (each
+  // lane of a 16-lane group names 4 consecutive columns of one row; lane j of
+  // the group receives column j of rows 4h .. 4h+3 of its 8).
+  const int q4 = lane >> 4, jl = lane & 15;
+  f32x4 oacc[CB];
 #pragma unroll
-    for (int i = 0; i < per_batch; ++i) {
-      const int t = min(tw + (bt * per_batch + i) * TPI, n - 1);
-      dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + (int64_t)t * row_stride));
-    }
-  };
-  // Weighted values.
-  float acc[GM][8];
-#pragma unroll
-  for (int g = 0; g < GM; ++g)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
+  for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-  for (int bt = 0; bt < nbatch; ++bt) {
-    u32x4 vv[per_batch];
-    load_batch(vv, vbase, bt);
+  for (int pass = 0; pass < NPASS; ++pass) {
+    if (pass > 0) {
+      barrier_no_fence();  // every wavefront is done reading the previous pass
+      issue_v(pass);
+    }
+    wait_vmcnt<0>();  // this wavefront's value rows have landed ...
+    wait_lgkmcnt0();
+    barrier_no_fence();  // ... and so have every other wavefront's (and the softmax)
+#pragma unroll 2
+    for (int ks = 0; ks < VS / 32; ++ks) {
+      const int tb = pass * VS + ks * 32 + 8 * q4;  // first token of this lane's 8
+      v8i16 pa = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (jl < G) {
+        const f32x4 p0 = *reinterpret_cast<const f32x4 *>(&ps[jl][tb]);
+        const f32x4 p1 = *reinterpret_cast<const f32x4 *>(&ps[jl][tb + 4]);
 #pragma unroll
-    for (int i = 0; i < per_batch; ++i) {
-      // p_t = exp(-inf) = 0 for t >= n, whose row is a copy of token n - 1
-      const int t = tw + (bt * per_batch + i) * TPI;
-      float vf[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        vf[2 * j] = lo_bf16(vv[i][j]);
-        vf[2 * j + 1] = hi_bf16(vv[i][j]);
+        for (int e = 0; e < 4; ++e) {
+          pa[e] = (short)f32_to_bf16_rne(p0[e]);
+          pa[4 + e] = (short)f32_to_bf16_rne(p1[e]);
+        }
       }
+      const bf16x8 A = __builtin_bit_cast(bf16x8, pa);
+      const int vrow = ks * 32 + 8 * q4 + (jl >> 2);
 #pragma unroll
-      for (int g = 0; g < GM; ++g) {
-        const float p = g < G ? ps[g][t] : 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = acc[g][e] + p * vf[e];
+      for (int cb = 0; cb < CB; ++cb) {
+        const int d0 = (wv * CB + cb) * 16 + 4 * (jl & 3);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16 *)(vs + vrow * D + d0));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16 *)(vs + (vrow + 4) * D + d0));
+        const v8i16 bb = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bb),
+                                                           oacc[cb], 0, 0, 0);
       }
     }
   }
-  // Lanes of one d slice (same dl, different tl) combine by xor over the
-  // token-lane offsets, then wavefront partials meet in LDS.
+  // Lane l holds O[g = 4(l >> 4) + v][d = block + (l & 15)].
 #pragma unroll
-  for (int g = 0; g < GM; ++g)
+  for (int cb = 0; cb < CB; ++cb) {
+    const int d = (wv * CB + cb) * 16 + jl;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int off = L; off < 64; off <<= 1) acc[g][e] = acc[g][e] + __shfl_xor(acc[g][e], off, 64);
-  if (tl == 0) {
-#pragma unroll
-    for (int g = 0; g < GM; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[wv][g][dl * 8 + e] = acc[g][e];
-  }
-  __syncthreads();
-  for (int pi = tid; pi < G * D; pi += kThreads) {
-    const int g = pi / D, d = pi % D;
-    const float a = ((red[0][g][d] + red[1][g][d]) + red[2][g][d]) + red[3][g][d];
-    wsb[(int64_t)g * nc_max * (D + 2) + d] = a;
+    for (int v = 0; v < 4; ++v) {
+      const int g = 4 * q4 + v;
+      if (g < G) wsb[(int64_t)g * nc_max * (D + 2) + d] = oacc[cb][v];
+    }
   }
 }
 
@@ -253,6 +272,7 @@ extern "C" int bi_decode_attention(const uint16_t *q, const uint16_t *k_cache,
   if (D != 64 && D != 128) return BI_ERR_UNSUPPORTED;
   if (H % Hkv || H / Hkv > kMaxG) return BI_ERR_UNSUPPORTED;
   if (split_size != 128 && split_size != 256 && split_size != 512) return BI_ERR_UNSUPPORTED;
+  if ((int64_t)split_size * Hkv * D * 2 > 0x7FFFFFFF) return BI_ERR_UNSUPPORTED;  // 32-bit offsets
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
       !aligned16(ws) || ((uintptr_t)lens & 3))
     return BI_ERR_ALIGN;
