@@ -15,14 +15,18 @@
 // workgroup owns.  The configuration is picked from (N, K) alone.
 //
 // Data path per workgroup (4 wavefronts, 2 x 2 over the tile):
-//   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS (ring of 4 stages of BK = 32)
+//   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS
 //          --ds_read_b128--> VGPR fragments --MFMA--> fp32 accumulators
 //   epilogue: accumulators -> bf16 (round to nearest even) -> 8-byte stores.
-// LDS rows are 64 bytes (32 bf16 of one matrix row); their four 16-byte
-// chunks are XOR-permuted by a function of the row so that the 32 rows a
-// fragment read touches spread over all LDS banks.  Rows beyond M (or N) are
-// loaded as copies of the last valid row and never stored, so no row's
-// arithmetic depends on how many rows the batch holds.
+// Two LDS staging schemes feed the same instruction sequence:
+//   * BK = 32 stages (any K % 32 == 0): 64-byte LDS rows, a ring of 4 stages;
+//   * BK = 64 stages (256 x 256 tiles when K % 64 == 0): whole 128-byte lines
+//     per row, so every L2 request is a full line; weights in a ring of 2
+//     stages and activations in a ring of 3 (160 KiB of LDS).
+// Each LDS row's 16-byte chunks are XOR-permuted by a function of the row so
+// that the 32 rows a fragment read touches spread over all LDS banks.  Rows
+// beyond M (or N) are loaded as copies of the last valid row and never
+// stored, so no row's arithmetic depends on how many rows the batch holds.
 #include "common.h"
 
 namespace bi {
@@ -247,6 +251,236 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[BN / 64][BM / 64], c
 
 }
 
+// Epilogue.  Accumulator block (i, j) of a wavefront, register v, holds
+// n = base_n + 8*(v/4) + 4*(lane/32) + v%4 and m = base_m + lane%32: four
+// consecutive n of one output row per group of 4 registers -> one 8-byte store.
+template <int BN, int BM>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[BN / 64][BM / 64], uint16_t *y,
+                                           int M, int N, int64_t ldy, int m0, int n0, int wn,
+                                           int wm, int lane) {
+  constexpr int WN = BN / 2, WM = BM / 2;
+#pragma unroll
+  for (int j = 0; j < BM / 64; ++j) {
+    const int m = m0 + wm * WM + j * 32 + (lane & 31);
+    if (m >= M) continue;
+    uint16_t *yrow = y + (int64_t)m * ldy;
+#pragma unroll
+    for (int i = 0; i < BN / 64; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * WN + i * 32 + q * 8 + (lane >> 5) * 4;
+        if (n < N) {
+          uint2 o;
+          o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+          o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+          *reinterpret_cast<uint2 *>(yrow + n) = o;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide-stage variant: BK = 64, so an LDS row is a whole 128-byte line of one
+// matrix row and each direct-to-LDS load instruction moves 8 full lines (one
+// 128-byte L2 request per line instead of two 64-byte ones).  Two stages fit
+// the LDS at 256 x 256; stage kb + 2 is issued once every wavefront has read
+// its last fragments of stage kb.  The k order is unchanged: 16-k matrix-core
+// steps, ascending, so the bits equal the BK = 32 kernel's.
+constexpr int BK2 = 64;
+constexpr int kRow2 = BK2 * 2;  // 128 bytes: eight 16-byte chunks
+
+// Chunk c of LDS row r is stored at c ^ swz2(r).  A fragment read touches 32
+// consecutive rows at one logical chunk; rows r and r + 1 share a 256-byte
+// window, so 16 consecutive rows cover the 16 bank groups exactly once.
+__device__ __forceinline__ int swz2(int row) { return (row >> 1) & 7; }
+
+template <int BN, int BM>
+struct Cfg2 {
+  static constexpr int WN = BN / 2, WM = BM / 2;
+  static constexpr int FN = WN / 32, FM = WM / 32;
+  static constexpr int W_BYTES = BN * kRow2;  // one weight stage
+  static constexpr int X_BYTES = BM * kRow2;  // one activation stage
+  static constexpr int LDS = 2 * W_BYTES + 3 * X_BYTES;
+  static constexpr int LW = BN / 32, LX = BM / 32;  // load instructions per wavefront per stage
+  static_assert(BN % 64 == 0 && BM % 64 == 0 && LW + 2 * LX < 64, "tile");
+};
+
+// Wavefront wv, instruction i fills LDS rows [i*32 + wv*8, +8): lane l writes
+// row (l >> 3), physical chunk (l & 7), i.e. logical chunk (l & 7) ^ swz2(row).
+template <int ROWS>
+struct LoadPlan2 {
+  static constexpr int N = ROWS / 32;
+  __amdgpu_buffer_rsrc_t rsrc;
+  int off[N];
+  __device__ __forceinline__ void init(const uint16_t *g, int rows_total, int row0, int row_limit,
+                                       int64_t ld, int K, int wv, int lane) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)g, (short)0,
+                                             (int)(((int64_t)(rows_total - 1) * ld + K) * 2),
+                                             0x00020000);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int r = i * 32 + wv * 8 + (lane >> 3);
+      int gr = row0 + r;
+      gr = gr < row_limit ? gr : row_limit - 1;
+      off[i] = ((int)(gr * ld) + (((lane & 7) ^ swz2(r)) << 3)) * 2;
+    }
+  }
+  // instructions [i0, i1) of a stage (compile-time bounds after inlining)
+  __device__ __forceinline__ void issue(char *lds, int k0, int wv, int i0 = 0, int i1 = N) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (i < i0 || i >= i1) continue;
+      lds_void *dst = (lds_void *)(lds + (i * 32 + wv * 8) * kRow2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, off[i], k0 * 2, 0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ bf16x8 read_frag2(const char *lds, int row, int ks, int lane) {
+  const int lc = ks * 2 + (lane >> 5);
+  return *reinterpret_cast<const bf16x8 *>(lds + row * kRow2 + ((lc ^ swz2(row)) << 4));
+}
+
+// Issued in the order the products consume them: a[0] with every b[j] comes
+// first, then a[1], a[2], ... -- the first product waits for two reads only.
+template <int BN, int BM>
+__device__ __forceinline__ void read_frags2(Frags<BN, BM> &f, const char *wl, const char *xl,
+                                            int ks, int wn, int wm, int lane) {
+  using C = Cfg2<BN, BM>;
+  f.a[0] = read_frag2(wl, wn * C::WN + (lane & 31), ks, lane);
+#pragma unroll
+  for (int j = 0; j < C::FM; ++j) f.b[j] = read_frag2(xl, wm * C::WM + j * 32 + (lane & 31), ks, lane);
+#pragma unroll
+  for (int i = 1; i < C::FN; ++i) f.a[i] = read_frag2(wl, wn * C::WN + i * 32 + (lane & 31), ks, lane);
+}
+
+// Scheduling hint: spread the NREAD fragment reads, then the NDMA loads,
+// evenly between the NMFMA matrix-core instructions of a step.
+template <int NMFMA, int NDMA, int NREAD>
+__device__ __forceinline__ void interleave_even() {
+  constexpr int NMEM = NDMA + NREAD;
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    const int t0 = i * NMEM / NMFMA, t1 = (i + 1) * NMEM / NMFMA;
+#pragma unroll
+    for (int t = t0; t < t1; ++t) {
+      if (t < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  }
+}
+
+// Steps 0..2 of a stage (fragments of steps 1..3 are read while the previous
+// step multiplies), with the activation loads of a later stage spread over
+// steps 0 and 1 when XLOAD.  Leaves step 3's fragments in f1.
+template <int BN, int BM, bool XLOAD>
+__device__ __forceinline__ void stage_head2(f32x16 (&acc)[BN / 64][BM / 64], Frags<BN, BM> &f0,
+                                            Frags<BN, BM> &f1, const char *wc, const char *xc,
+                                            const LoadPlan2<BM> &px, char *xdst, int k0, int wn,
+                                            int wm, int wv, int lane) {
+  using C = Cfg2<BN, BM>;
+  constexpr int H = C::LX / 2;
+  read_frags2<BN, BM>(f1, wc, xc, 1, wn, wm, lane);
+  if (XLOAD) px.issue(xdst, k0, wv, 0, H);
+  mfma_step<BN, BM>(acc, f0);
+  interleave_even<C::FN * C::FM, XLOAD ? H : 0, C::FN + C::FM>();
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags2<BN, BM>(f0, wc, xc, 2, wn, wm, lane);
+  if (XLOAD) px.issue(xdst, k0, wv, H, C::LX);
+  mfma_step<BN, BM>(acc, f1);
+  interleave_even<C::FN * C::FM, XLOAD ? C::LX - H : 0, C::FN + C::FM>();
+  __builtin_amdgcn_sched_barrier(0);
+  read_frags2<BN, BM>(f1, wc, xc, 3, wn, wm, lane);
+  mfma_step<BN, BM>(acc, f0);
+  interleave_even<C::FN * C::FM, 0, C::FN + C::FM>();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Weights in a ring of 2 stages, activations in a ring of 3.  In stage kb the
+// activations of stage kb + 2 load during the first steps (their slot held
+// stage kb - 1); the weights of stage kb + 2 load after the end-of-stage
+// barrier, once every wavefront has read stage kb.
+template <int BN, int BM>
+__device__ __forceinline__ void gemm_mainloop2(f32x16 (&acc)[BN / 64][BM / 64], char *lds,
+                                               const uint16_t *__restrict__ x,
+                                               const uint16_t *__restrict__ w, int M, int N,
+                                               int nkb, int64_t ldx, int64_t ldw, int m0, int n0,
+                                               int wv, int lane, int kspan) {
+  using C = Cfg2<BN, BM>;
+  const int wn = wv >> 1, wm = wv & 1;
+  LoadPlan2<BN> pw;
+  LoadPlan2<BM> px;
+  pw.init(w, N, n0, N, ldw, kspan, wv, lane);
+  px.init(x, M, m0, M, ldx, kspan, wv, lane);
+#pragma unroll
+  for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
+
+  char *wa = lds, *wb = lds + C::W_BYTES;            // weight slots: current, next
+  char *xa = lds + 2 * C::W_BYTES;                   // activation slots: current, next, free
+  char *xb = xa + C::X_BYTES, *xf = xb + C::X_BYTES;
+  pw.issue(wa, 0, wv);
+  px.issue(xa, 0, wv);
+  if (nkb > 1) {
+    pw.issue(wb, BK2, wv);
+    px.issue(xb, BK2, wv);
+    wait_vmcnt<C::LW + C::LX>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  barrier_no_fence();
+
+  Frags<BN, BM> f0, f1;
+  read_frags2<BN, BM>(f0, wa, xa, 0, wn, wm, lane);
+  int kb = 0;
+  for (; kb + 2 < nkb; ++kb) {
+    stage_head2<BN, BM, true>(acc, f0, f1, wa, xa, px, xf, (kb + 2) * BK2, wn, wm, wv, lane);
+    wait_lgkmcnt0();
+    wait_vmcnt<C::LX>();  // stage kb + 1 has landed; stage kb + 2's activations may fly
+    barrier_no_fence();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags2<BN, BM>(f0, wb, xb, 0, wn, wm, lane);
+    pw.issue(wa, (kb + 2) * BK2, wv);
+    mfma_step<BN, BM>(acc, f1);
+    interleave_even<C::FN * C::FM, C::LW, C::FN + C::FM>();
+    __builtin_amdgcn_sched_barrier(0);
+    char *t = wa; wa = wb; wb = t;
+    t = xa; xa = xb; xb = xf; xf = t;
+  }
+  if (kb + 1 < nkb) {
+    stage_head2<BN, BM, false>(acc, f0, f1, wa, xa, px, xf, 0, wn, wm, wv, lane);
+    wait_lgkmcnt0();
+    wait_vmcnt<0>();
+    barrier_no_fence();
+    read_frags2<BN, BM>(f0, wb, xb, 0, wn, wm, lane);
+    mfma_step<BN, BM>(acc, f1);
+    wa = wb;
+    xa = xb;
+  }
+  stage_head2<BN, BM, false>(acc, f0, f1, wa, xa, px, xf, 0, wn, wm, wv, lane);
+  mfma_step<BN, BM>(acc, f1);
+}
+
+template <int BN, int BM>
+__global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+  using C = Cfg2<BN, BM>;
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wv >> 1, wm = wv & 1;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int n0 = tn * BN, m0 = tm * BM;
+  f32x16 acc[C::FN][C::FM];
+  gemm_mainloop2<BN, BM>(acc, lds, x, w, M, N, K / BK2, ldx, ldw, m0, n0, wv, lane, K);
+  store_tile<BN, BM>(acc, y, M, N, ldy, m0, n0, wn, wm, lane);
+}
+
 template <int BN, int BM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
@@ -263,29 +497,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 
   f32x16 acc[C::FN][C::FM];
   gemm_mainloop<BN, BM>(acc, lds, x, w, M, N, K / BK, ldx, ldw, m0, n0, wv, lane, K);
-
-  // Epilogue.  Accumulator block (i, j) of this wavefront, register v, holds
-  // n = base_n + 8*(v/4) + 4*(lane/32) + v%4 and m = base_m + lane%32: four
-  // consecutive n of one output row per group of 4 registers -> one 8-byte store.
-#pragma unroll
-  for (int j = 0; j < C::FM; ++j) {
-    const int m = m0 + wm * C::WM + j * 32 + (lane & 31);
-    if (m >= M) continue;
-    uint16_t *yrow = y + (int64_t)m * ldy;
-#pragma unroll
-    for (int i = 0; i < C::FN; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * C::WN + i * 32 + q * 8 + (lane >> 5) * 4;
-        if (n < N) {
-          uint2 o;
-          o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-          o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-          *reinterpret_cast<uint2 *>(yrow + n) = o;
-        }
-      }
-    }
-  }
+  store_tile<BN, BM>(acc, y, M, N, ldy, m0, n0, wn, wm, lane);
 }
 
 // Split-K partial tile: blockIdx.y = chunk s covers k in [s*kc, (s+1)*kc).
@@ -353,17 +565,19 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_combine_kernel(
   *reinterpret_cast<u32x4 *>(y + m * ldy + n) = o;
 }
 
+typedef void (*GemmKernel)(const uint16_t *, const uint16_t *, uint16_t *, int, int, int, int64_t,
+                           int64_t, int64_t, int, int);
 struct CfgEntry {
   int bn, bm;
-  void (*kernel)(const uint16_t *, const uint16_t *, uint16_t *, int, int, int, int64_t,
-                 int64_t, int64_t, int, int);
+  GemmKernel kernel;  // BK = 32 stages, any K % 32 == 0
+  GemmKernel wide;    // BK = 64 stages, used when K % 64 == 0 (same k order, same bits)
 };
 
 const CfgEntry kConfigs[] = {
-    {256, 256, gemm_kernel<256, 256>},
-    {256, 128, gemm_kernel<256, 128>},
-    {128, 128, gemm_kernel<128, 128>},
-    {128, 256, gemm_kernel<128, 256>},
+    {256, 256, gemm_kernel<256, 256>, gemm_wide_kernel<256, 256>},
+    {256, 128, gemm_kernel<256, 128>, nullptr},
+    {128, 128, gemm_kernel<128, 128>, nullptr},
+    {128, 256, gemm_kernel<128, 256>, nullptr},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -408,7 +622,8 @@ int launch(int cfg, const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M
   const CfgEntry &c = kConfigs[cfg];
   const int64_t tiles_m = (M + c.bm - 1) / c.bm, tiles_n = (N + c.bn - 1) / c.bn;
   if (tiles_m * tiles_n > 0x7FFFFFFF) return BI_ERR_SHAPE;
-  hipLaunchKernelGGL(c.kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0,
+  const GemmKernel kern = (c.wide && K % BK2 == 0) ? c.wide : c.kernel;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0,
                      (hipStream_t)stream, x, w, y, (int)M, (int)N, (int)K, ldx, ldw, ldy,
                      (int)tiles_m, (int)tiles_n);
   return launch_status();
