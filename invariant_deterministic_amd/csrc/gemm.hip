@@ -251,32 +251,56 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[BN / 64][BM / 64], c
 
 }
 
-// Epilogue.  Accumulator block (i, j) of a wavefront, register v, holds
-// n = base_n + 8*(v/4) + 4*(lane/32) + v%4 and m = base_m + lane%32: four
-// consecutive n of one output row per group of 4 registers -> one 8-byte store.
+// Epilogue through LDS, so that every global store writes whole 128-byte
+// lines (per-lane 8-byte stores straight from the accumulators would issue
+// eight partial-line requests per line and, with every tile finishing at the
+// same moment, stall on the L2 request rate).
+//
+// Accumulator block (i, j) of a wavefront, register v, holds
+// n = 32i + 8(v/4) + 4(lane/32) + v%4 and m = 32j + lane%32 of the
+// wavefront's WN x WM sub-tile.  Each wavefront writes its sub-tile, rounded
+// to bf16, to its own LDS region as rows of m (WN bf16 = CH 16-byte chunks,
+// chunk c of row m stored at c ^ f(m)), then reads it back 16 bytes per lane,
+// eight lanes per 128-byte row segment, and stores those segments.  f spreads
+// the 32 rows of one accumulator write over the banks and gives two adjacent
+// rows disjoint chunk sets for the reads.  The caller has made the LDS free.
 template <int BN, int BM>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[BN / 64][BM / 64], uint16_t *y,
-                                           int M, int N, int64_t ldy, int m0, int n0, int wn,
-                                           int wm, int lane) {
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[BN / 64][BM / 64], char *lds,
+                                           uint16_t *y, int M, int N, int64_t ldy, int m0, int n0,
+                                           int wn, int wm, int wv, int lane) {
   constexpr int WN = BN / 2, WM = BM / 2;
+  constexpr int CH = WN / 8;          // 16-byte chunks per LDS row
+  constexpr int ROWB = WN * 2;        // bytes per LDS row
+  constexpr int HB = CH / 2;
+  static_assert(CH == 8 || CH == 16, "sub-tile width");
+  char *mine = lds + wv * (WM * ROWB);
+  auto f = [](int m) { return ((m & 1) * HB) | ((m >> 1) & (HB - 1)); };
 #pragma unroll
   for (int j = 0; j < BM / 64; ++j) {
-    const int m = m0 + wm * WM + j * 32 + (lane & 31);
-    if (m >= M) continue;
-    uint16_t *yrow = y + (int64_t)m * ldy;
+    const int m = j * 32 + (lane & 31);
+    char *row = mine + m * ROWB + (lane >> 5) * 8;
+    const int fm = f(m);
 #pragma unroll
     for (int i = 0; i < BN / 64; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WN + i * 32 + q * 8 + (lane >> 5) * 4;
-        if (n < N) {
-          uint2 o;
-          o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-          o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-          *reinterpret_cast<uint2 *>(yrow + n) = o;
-        }
+        uint2 o;
+        o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+        o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+        *reinterpret_cast<uint2 *>(row + (((i * 4 + q) ^ fm) << 4)) = o;
       }
     }
+  }
+  // A wavefront's LDS operations complete in order: its reads below see its
+  // writes above.
+  constexpr int SEG = CH / 8;  // 128-byte segments per row
+#pragma unroll 4
+  for (int t = 0; t < WM / 8 * SEG; ++t) {
+    const int r = (t / SEG) * 8 + (lane >> 3);
+    const int c = (t % SEG) * 8 + (lane & 7);
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(mine + r * ROWB + ((c ^ f(r)) << 4));
+    const int m = m0 + wm * WM + r, n = n0 + wn * WN + c * 8;
+    if (m < M && n < N) *reinterpret_cast<u32x4 *>(y + (int64_t)m * ldy + n) = v;
   }
 }
 
@@ -478,7 +502,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
   const int n0 = tn * BN, m0 = tm * BM;
   f32x16 acc[C::FN][C::FM];
   gemm_mainloop2<BN, BM>(acc, lds, x, w, M, N, K / BK2, ldx, ldw, m0, n0, wv, lane, K);
-  store_tile<BN, BM>(acc, y, M, N, ldy, m0, n0, wn, wm, lane);
+  barrier_no_fence();  // every wavefront is done reading the stages
+  store_tile<BN, BM>(acc, lds, y, M, N, ldy, m0, n0, wn, wm, wv, lane);
 }
 
 template <int BN, int BM>
@@ -497,7 +522,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 
   f32x16 acc[C::FN][C::FM];
   gemm_mainloop<BN, BM>(acc, lds, x, w, M, N, K / BK, ldx, ldw, m0, n0, wv, lane, K);
-  store_tile<BN, BM>(acc, y, M, N, ldy, m0, n0, wn, wm, lane);
+  barrier_no_fence();  // every wavefront is done reading the stages
+  store_tile<BN, BM>(acc, lds, y, M, N, ldy, m0, n0, wn, wm, wv, lane);
 }
 
 // Split-K partial tile: blockIdx.y = chunk s covers k in [s*kc, (s+1)*kc).
