@@ -185,15 +185,14 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
 #pragma unroll 2
     for (int ks = 0; ks < VS / 32; ++ks) {
       const int tb = pass * VS + ks * 32 + 8 * q4;  // first token of this lane's 8
-      v8i16 pa = {0, 0, 0, 0, 0, 0, 0, 0};
+      u32x4 pa = {0u, 0u, 0u, 0u};
       if (jl < G) {
         const f32x4 p0 = *reinterpret_cast<const f32x4 *>(&ps[jl][tb]);
         const f32x4 p1 = *reinterpret_cast<const f32x4 *>(&ps[jl][tb + 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pa[e] = (short)f32_to_bf16_rne(p0[e]);
-          pa[4 + e] = (short)f32_to_bf16_rne(p1[e]);
-        }
+        pa[0] = pack_bf16x2(p0[0], p0[1]);
+        pa[1] = pack_bf16x2(p0[2], p0[3]);
+        pa[2] = pack_bf16x2(p1[0], p1[1]);
+        pa[3] = pack_bf16x2(p1[2], p1[3]);
       }
       const bf16x8 A = __builtin_bit_cast(bf16x8, pa);
       const int vrow = ks * 32 + 8 * q4 + (jl >> 2);

@@ -13,17 +13,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// fp32 -> bf16 bit pattern, round to nearest, ties to even, written with
-// integer operations so that the rounding is exactly the format's definition:
-// add half an output ulp minus one, plus the output lsb (which turns an exact
-// tie into a round-up only when the kept part is odd), then truncate.  NaN is
-// returned as a quiet NaN with its sign.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 bit patterns in one word (lo in the low half), round
+// to nearest, ties to even, NaN returned quiet with its sign: one
+// v_cvt_pk_bf16_f32.  Its result equals, for every one of the 2^32 fp32 bit
+// patterns (checked exhaustively on gfx950), the format's integer
+// definition: add half an output ulp minus one plus the kept lsb, truncate;
+// NaN -> (bits >> 16) | 0x40.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t quiet = (u >> 16) | 0x0040u;
-  // a select, not a branch: the conversion sits in the stores of every kernel
-  return (uint16_t)((u & 0x7FFFFFFFu) > 0x7F800000u ? quiet : rounded);
+  return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 
 // bf16 bit pattern -> fp32 (exact).
@@ -34,10 +39,6 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) {
 // Two bf16 in one 32-bit word (low half first) -> fp32.
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
-}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
