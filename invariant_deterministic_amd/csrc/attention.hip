@@ -221,6 +221,13 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
   }
 }
 
+// Chunk combine for one (head, sequence); thread d owns output column d.
+// The order is that of the header: M = max over chunks (exact), then L and
+// O[d] summed over chunks c ascending with weights exp(m_c - M).  The loads
+// are batched so the loop costs a memory round trip per kCT chunks, not two
+// per chunk: chunk statistics go through LDS, kCT rows of values are loaded
+// before they are summed.
+constexpr int kCT = 16;
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float *__restrict__ ws,
                                                          const int32_t *__restrict__ lens,
@@ -231,13 +238,41 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float *__restrict
   T = T < 1 ? 1 : (T > Tmax ? Tmax : T);
   const int nc = (T + C - 1) / C;
   const float *p = ws + ((int64_t)b * H + h) * nc_max * (D + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, p[(int64_t)c * (D + 2) + D]);
+  constexpr int S = D + 2;  // floats per chunk record
+
+  // M: every thread takes the max over its chunks, then a max over threads
+  // (max is exact, so the grouping does not matter).
+  __shared__ float red[D / 64];
+  float m = -INFINITY;
+  for (int c = d; c < nc; c += D) m = fmaxf(m, p[(int64_t)c * S + D]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((d & 63) == 0) red[d >> 6] = m;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int i = 1; i < D / 64; ++i) M = fmaxf(M, red[i]);
+
+  __shared__ float fw[kCT], lw[kCT];
   float L = 0.0f, O = 0.0f;
-  for (int c = 0; c < nc; ++c) {
-    const float f = expf(p[(int64_t)c * (D + 2) + D] - M);
-    L = L + f * p[(int64_t)c * (D + 2) + D + 1];
-    O = O + f * p[(int64_t)c * (D + 2) + d];
+  for (int c0 = 0; c0 < nc; c0 += kCT) {
+    const int n = min(kCT, nc - c0);
+    __syncthreads();  // the previous tile's fw / lw are consumed
+    if (d < n) {
+      fw[d] = expf(p[(int64_t)(c0 + d) * S + D] - M);
+      lw[d] = p[(int64_t)(c0 + d) * S + D + 1];
+    }
+    float a[kCT];
+#pragma unroll
+    for (int i = 0; i < kCT; ++i) a[i] = i < n ? p[(int64_t)(c0 + i) * S + d] : 0.0f;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kCT; ++i) {
+      if (i < n) {
+        L = L + fw[i] * lw[i];
+        O = O + fw[i] * a[i];
+      }
+    }
   }
   o[((int64_t)b * H + h) * D + d] = f32_to_bf16_rne(O / L);
 }
