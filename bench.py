@@ -340,6 +340,25 @@ def sweep(path, bi, torch, dev, to_dev):
                       f"({recs[-1]['gbs']:.0f} GB/s) vs bi_gemm {ms*1e3:.1f} us",
                       file=sys.stderr, flush=True)
         del W, Ws, xpool
+    # The 70B MLP shape of the dynamic-batch stream (K = 8192, N = 28672, W 448 MiB)
+    c70 = workloads.LLAMA70B
+    W = to_dev(workloads.llama70b_w())
+    xpool = to_dev(workloads.llama70b_x_pool())
+    K, N = c70["K"], c70["N"]
+    for M in (1, 64, 1024, 2048, 4096):
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ms = _time_loop(torch, lambda i: bi.bi_gemm(xpool[:M], W, y=y), 10)
+        fl = 2.0 * M * N * K
+        by = 2.0 * (M * K + N * K + M * N)
+        t_roof = max(fl / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
+        recs.append({"kernel": "bi_gemm", "K": K, "N": N, "M": M, "us": ms * 1e3,
+                     "tflops": fl / (ms * 1e-3) / 1e12, "gbs": by / (ms * 1e-3) / 1e9,
+                     "frac_mfma": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "frac_roofline": t_roof / (ms * 1e-3),
+                     "config": bi.bi_gemm_config_id(N, K)})
+        print(f"# sweep gemm K={K} N={N} M={M}: {recs[-1]['tflops']:.1f} TFLOP/s "
+              f"({ms*1e3:.1f} us)", file=sys.stderr, flush=True)
+    del W, xpool
     # Reference: a plain device copy (torch) of the same bytes as RMSNorm at
     # M = 2048 / 8192 and of 512 MiB -- the practical read+write rate of HBM
     # on this part, beside the 8 TB/s spec.

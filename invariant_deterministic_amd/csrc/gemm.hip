@@ -20,9 +20,9 @@
 //   epilogue: accumulators -> bf16 (round to nearest even) -> 8-byte stores.
 // Two LDS staging schemes feed the same instruction sequence:
 //   * BK = 32 stages (any K % 32 == 0): 64-byte LDS rows, a ring of 4 stages;
-//   * BK = 64 stages (256 x 256 tiles when K % 64 == 0): whole 128-byte lines
-//     per row, so every L2 request is a full line; weights in a ring of 2
-//     stages and activations in a ring of 3 (160 KiB of LDS).
+//   * BK = 64 stages (every tile shape, when K % 64 == 0): whole 128-byte
+//     lines per row, so every L2 request is a full line; weights in a ring of
+//     2 stages and activations in a ring of 3 (160 KiB of LDS at 256 x 256).
 // Each LDS row's 16-byte chunks are XOR-permuted by a function of the row so
 // that the 32 rows a fragment read touches spread over all LDS banks.  Rows
 // beyond M (or N) are loaded as copies of the last valid row and never
@@ -601,9 +601,9 @@ struct CfgEntry {
 
 const CfgEntry kConfigs[] = {
     {256, 256, gemm_kernel<256, 256>, gemm_wide_kernel<256, 256>},
-    {256, 128, gemm_kernel<256, 128>, nullptr},
-    {128, 128, gemm_kernel<128, 128>, nullptr},
-    {128, 256, gemm_kernel<128, 256>, nullptr},
+    {256, 128, gemm_kernel<256, 128>, gemm_wide_kernel<256, 128>},
+    {128, 128, gemm_kernel<128, 128>, gemm_wide_kernel<128, 128>},
+    {128, 256, gemm_kernel<128, 256>, gemm_wide_kernel<128, 256>},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 

@@ -174,18 +174,38 @@ def test_gemm_strided_and_m_zero(bi):
     bi.bi_gemm(X[:0, :1024], Wt[:, :1024])
 
 
-@pytest.mark.parametrize("K", [64, 96, 128, 192, 256, 320, 1056])
-def test_gemm_wide_and_narrow_stages_agree(bi, K):
-    """Configuration 0 runs 64-k LDS stages when K % 64 == 0 and 32-k stages
-    otherwise; configuration 2 always runs 32-k stages.  Short K loops (one,
-    two, three stages) and ragged M and N edges give the same bits either way,
-    within tolerance of the oracle."""
+@pytest.mark.parametrize("K", [64, 128, 192, 256, 320])
+def test_gemm_wide_stages_short_k(bi, K):
+    """K % 64 == 0 runs 64-k LDS stages: loops of one, two, three stages and
+    ragged M and N edges give the same bits in every configuration, within
+    tolerance of the oracle."""
     M, N = 300, 520
     x = synth.normal_bf16((M, K), 97 + K)
     w = synth.normal_bf16((N, K), 98 + K)
     X, Wt = dev_bf16(x), dev_bf16(w)
-    say(f"gemm wide/narrow K={K}")
+    say(f"gemm wide K={K}")
     y0 = host_u16(bi.bi_gemm_with_config(0, X, Wt))
-    y2 = host_u16(bi.bi_gemm_with_config(2, X, Wt))
-    assert np.array_equal(y0, y2)
-    check_bf16(y0, oracle.gemm(x, w), f"wide/narrow K={K}")
+    for cfg in range(1, bi.bi_gemm_num_configs()):
+        assert np.array_equal(host_u16(bi.bi_gemm_with_config(cfg, X, Wt)), y0), cfg
+    check_bf16(y0, oracle.gemm(x, w), f"wide K={K}")
+
+
+@pytest.mark.parametrize("K", [32, 96, 1056])
+def test_gemm_wide_and_narrow_stages_agree(bi, K):
+    """K % 64 == 32 runs 32-k LDS stages.  Appending 32 zero columns to x and
+    w (K + 32, a multiple of 64, so 64-k stages) adds exact zeros after the
+    same ascending k steps: the two staging schemes must give the same bits,
+    in every configuration."""
+    M, N = 300, 520
+    x = synth.normal_bf16((M, K), 99 + K)
+    w = synth.normal_bf16((N, K), 100 + K)
+    xp = np.zeros((M, K + 32), np.uint16)
+    wp = np.zeros((N, K + 32), np.uint16)
+    xp[:, :K], wp[:, :K] = x, w
+    X, Wt, XP, WP = dev_bf16(x), dev_bf16(w), dev_bf16(xp), dev_bf16(wp)
+    say(f"gemm narrow K={K} vs wide K={K + 32}")
+    for cfg in range(bi.bi_gemm_num_configs()):
+        narrow = host_u16(bi.bi_gemm_with_config(cfg, X, Wt))
+        wide = host_u16(bi.bi_gemm_with_config(cfg, XP, WP))
+        assert np.array_equal(narrow, wide), cfg
+    check_bf16(narrow, oracle.gemm(x, w), f"narrow K={K}")
