@@ -529,12 +529,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
 // Split-K partial tile: blockIdx.y = chunk s covers k in [s*kc, (s+1)*kc).
 // The same K loop as gemm_kernel over that range; the fp32 sums go to
 // ws[s][m][n] (row stride N), four consecutive n per 16-byte store.
-template <int BN, int BM>
+// WIDE: 64-k stages (kc % 64 == 0), else 32-k stages.
+template <int BN, int BM, bool WIDE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_partial_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, float *__restrict__ ws,
     int M, int N, int kc, int64_t ldx, int64_t ldw, int tiles_m, int tiles_n) {
   using C = Cfg<BN, BM>;
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * C::STAGE];
+  constexpr int LDS_BYTES = WIDE ? Cfg2<BN, BM>::LDS : kStages * C::STAGE;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -545,8 +547,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_partial_kernel(
   const int s = blockIdx.y;
 
   f32x16 acc[C::FN][C::FM];
-  gemm_mainloop<BN, BM>(acc, lds, x + (int64_t)s * kc, w + (int64_t)s * kc, M, N, kc / BK, ldx,
-                        ldw, m0, n0, wv, lane, kc);
+  if constexpr (WIDE)
+    gemm_mainloop2<BN, BM>(acc, lds, x + (int64_t)s * kc, w + (int64_t)s * kc, M, N, kc / BK2, ldx,
+                           ldw, m0, n0, wv, lane, kc);
+  else
+    gemm_mainloop<BN, BM>(acc, lds, x + (int64_t)s * kc, w + (int64_t)s * kc, M, N, kc / BK, ldx,
+                          ldw, m0, n0, wv, lane, kc);
 
   float *part = ws + (int64_t)s * M * N;
 #pragma unroll
@@ -713,10 +719,15 @@ extern "C" int bi_gemm_splitk(const uint16_t *x, const uint16_t *w, uint16_t *y,
   if (tiles_m * tiles_n > 0x7FFFFFFF) return BI_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   float *wsf = static_cast<float *>(ws);
-  hipLaunchKernelGGL((gemm_partial_kernel<kSplitBN, kSplitBM>),
-                     dim3((unsigned)(tiles_m * tiles_n), (unsigned)split_k), dim3(kThreads), 0, s,
-                     x, w, wsf, (int)M, (int)N, (int)(K / split_k), ldx, ldw, (int)tiles_m,
-                     (int)tiles_n);
+  const int kc = (int)(K / split_k);
+  if (kc % BK2 == 0)
+    hipLaunchKernelGGL((gemm_partial_kernel<kSplitBN, kSplitBM, true>),
+                       dim3((unsigned)(tiles_m * tiles_n), (unsigned)split_k), dim3(kThreads), 0, s,
+                       x, w, wsf, (int)M, (int)N, kc, ldx, ldw, (int)tiles_m, (int)tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_partial_kernel<kSplitBN, kSplitBM, false>),
+                       dim3((unsigned)(tiles_m * tiles_n), (unsigned)split_k), dim3(kThreads), 0, s,
+                       x, w, wsf, (int)M, (int)N, kc, ldx, ldw, (int)tiles_m, (int)tiles_n);
   if ((st = launch_status()) != BI_OK) return st;
   const int64_t groups = (M * N / 8 + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(gemm_splitk_combine_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, wsf,

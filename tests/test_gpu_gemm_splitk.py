@@ -45,8 +45,11 @@ def _pin_inputs(name, rows=5, n=16, col=3):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1024, 1024), (37, 520, 4096), (64, 4096, 4096),
-                                   (130, 264, 14336)])
+                                   (130, 264, 14336), (37, 520, 2112)])
 def test_splitk_integer_inputs_bitwise(bi, M, N, K):
+    """Exact in every order.  Chunks of K / S with K / S % 64 == 0 run 64-k
+    LDS stages, the others 32-k stages (K = 2112: S = 1 and S = 2 take one
+    path each)."""
     x = synth.int_bf16((M, K), M + 7, -4, 4)
     w = synth.int_bf16((N, K), N + 7, -4, 4)
     want = oracle.bf16_round(oracle.gemm(x, w))
