@@ -325,7 +325,6 @@ struct Cfg2 {
   static constexpr int FN = WN / 32, FM = WM / 32;
   static constexpr int W_BYTES = BN * kRow2;  // one weight stage
   static constexpr int X_BYTES = BM * kRow2;  // one activation stage
-  static constexpr int LDS = 2 * W_BYTES + 3 * X_BYTES;
   static constexpr int LW = BN / 32, LX = BM / 32;  // load instructions per wavefront per stage
   static_assert(BN % 64 == 0 && BM % 64 == 0 && LW + 2 * LX < 64, "tile");
 };
@@ -397,24 +396,25 @@ __device__ __forceinline__ void interleave_even() {
 }
 
 // Steps 0..2 of a stage (fragments of steps 1..3 are read while the previous
-// step multiplies), with the activation loads of a later stage spread over
-// steps 0 and 1 when XLOAD.  Leaves step 3's fragments in f1.
-template <int BN, int BM, bool XLOAD>
+// step multiplies), with the loads of a later stage of the operand that has
+// the ring of 3 spread over steps 0 and 1 when LOAD.  Leaves step 3's
+// fragments in f1.
+template <int BN, int BM, int ER, bool LOAD>
 __device__ __forceinline__ void stage_head2(f32x16 (&acc)[BN / 64][BM / 64], Frags<BN, BM> &f0,
                                             Frags<BN, BM> &f1, const char *wc, const char *xc,
-                                            const LoadPlan2<BM> &px, char *xdst, int k0, int wn,
+                                            const LoadPlan2<ER> &pe, char *edst, int k0, int wn,
                                             int wm, int wv, int lane) {
   using C = Cfg2<BN, BM>;
-  constexpr int H = C::LX / 2;
+  constexpr int LE = ER / 32, H = LE / 2;
   read_frags2<BN, BM>(f1, wc, xc, 1, wn, wm, lane);
-  if (XLOAD) px.issue(xdst, k0, wv, 0, H);
+  if (LOAD) pe.issue(edst, k0, wv, 0, H);
   mfma_step<BN, BM>(acc, f0);
-  interleave_even<C::FN * C::FM, XLOAD ? H : 0, C::FN + C::FM>();
+  interleave_even<C::FN * C::FM, LOAD ? H : 0, C::FN + C::FM>();
   __builtin_amdgcn_sched_barrier(0);
   read_frags2<BN, BM>(f0, wc, xc, 2, wn, wm, lane);
-  if (XLOAD) px.issue(xdst, k0, wv, H, C::LX);
+  if (LOAD) pe.issue(edst, k0, wv, H, LE);
   mfma_step<BN, BM>(acc, f1);
-  interleave_even<C::FN * C::FM, XLOAD ? C::LX - H : 0, C::FN + C::FM>();
+  interleave_even<C::FN * C::FM, LOAD ? LE - H : 0, C::FN + C::FM>();
   __builtin_amdgcn_sched_barrier(0);
   read_frags2<BN, BM>(f1, wc, xc, 3, wn, wm, lane);
   mfma_step<BN, BM>(acc, f0);
@@ -422,11 +422,20 @@ __device__ __forceinline__ void stage_head2(f32x16 (&acc)[BN / 64][BM / 64], Fra
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Weights in a ring of 2 stages, activations in a ring of 3.  In stage kb the
-// activations of stage kb + 2 load during the first steps (their slot held
-// stage kb - 1); the weights of stage kb + 2 load after the end-of-stage
-// barrier, once every wavefront has read stage kb.
-template <int BN, int BM>
+// LDS bytes of the 64-k scheme: one operand in a ring of 3 stages, the other
+// in a ring of 2 (W3: the weights have the ring of 3).
+template <int BN, int BM, bool W3>
+constexpr int wide_lds_bytes() {
+  return W3 ? 3 * BN * kRow2 + 2 * BM * kRow2 : 2 * BN * kRow2 + 3 * BM * kRow2;
+}
+
+// One operand in a ring of 3 stages, the other in a ring of 2.  In stage kb
+// the ring-of-3 operand's stage kb + 2 loads during the first steps (its slot
+// held stage kb - 1); the ring-of-2 operand's stage kb + 2 loads after the
+// end-of-stage barrier, once every wavefront has read stage kb.  Activations
+// take the ring of 3 in the full-size kernels (W3 = false); the small-M
+// split-K partials give it to the weights, whose read dominates there.
+template <int BN, int BM, bool W3>
 __device__ __forceinline__ void gemm_mainloop2(f32x16 (&acc)[BN / 64][BM / 64], char *lds,
                                                const uint16_t *__restrict__ x,
                                                const uint16_t *__restrict__ w, int M, int N,
@@ -443,9 +452,10 @@ __device__ __forceinline__ void gemm_mainloop2(f32x16 (&acc)[BN / 64][BM / 64], 
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
 
-  char *wa = lds, *wb = lds + C::W_BYTES;            // weight slots: current, next
-  char *xa = lds + 2 * C::W_BYTES;                   // activation slots: current, next, free
-  char *xb = xa + C::X_BYTES, *xf = xb + C::X_BYTES;
+  constexpr int NW = W3 ? 3 : 2;
+  // slots: current, next, free (the free slot only for the ring of 3)
+  char *wa = lds, *wb = wa + C::W_BYTES, *wf = wb + C::W_BYTES;
+  char *xa = lds + NW * C::W_BYTES, *xb = xa + C::X_BYTES, *xf = xb + C::X_BYTES;
   pw.issue(wa, 0, wv);
   px.issue(xa, 0, wv);
   if (nkb > 1) {
@@ -461,21 +471,33 @@ __device__ __forceinline__ void gemm_mainloop2(f32x16 (&acc)[BN / 64][BM / 64], 
   read_frags2<BN, BM>(f0, wa, xa, 0, wn, wm, lane);
   int kb = 0;
   for (; kb + 2 < nkb; ++kb) {
-    stage_head2<BN, BM, true>(acc, f0, f1, wa, xa, px, xf, (kb + 2) * BK2, wn, wm, wv, lane);
+    const int k2 = (kb + 2) * BK2;
+    if constexpr (W3)
+      stage_head2<BN, BM, BN, true>(acc, f0, f1, wa, xa, pw, wf, k2, wn, wm, wv, lane);
+    else
+      stage_head2<BN, BM, BM, true>(acc, f0, f1, wa, xa, px, xf, k2, wn, wm, wv, lane);
     wait_lgkmcnt0();
-    wait_vmcnt<C::LX>();  // stage kb + 1 has landed; stage kb + 2's activations may fly
+    // stage kb + 1 has landed; stage kb + 2 of the ring-of-3 operand may fly
+    wait_vmcnt<W3 ? C::LW : C::LX>();
     barrier_no_fence();
     __builtin_amdgcn_sched_barrier(0);
     read_frags2<BN, BM>(f0, wb, xb, 0, wn, wm, lane);
-    pw.issue(wa, (kb + 2) * BK2, wv);
+    if constexpr (W3) px.issue(xa, k2, wv);
+    else pw.issue(wa, k2, wv);
     mfma_step<BN, BM>(acc, f1);
-    interleave_even<C::FN * C::FM, C::LW, C::FN + C::FM>();
+    interleave_even<C::FN * C::FM, W3 ? C::LX : C::LW, C::FN + C::FM>();
     __builtin_amdgcn_sched_barrier(0);
-    char *t = wa; wa = wb; wb = t;
-    t = xa; xa = xb; xb = xf; xf = t;
+    char *t;
+    if constexpr (W3) {
+      t = wa; wa = wb; wb = wf; wf = t;
+      t = xa; xa = xb; xb = t;
+    } else {
+      t = wa; wa = wb; wb = t;
+      t = xa; xa = xb; xb = xf; xf = t;
+    }
   }
   if (kb + 1 < nkb) {
-    stage_head2<BN, BM, false>(acc, f0, f1, wa, xa, px, xf, 0, wn, wm, wv, lane);
+    stage_head2<BN, BM, BM, false>(acc, f0, f1, wa, xa, px, xf, 0, wn, wm, wv, lane);
     wait_lgkmcnt0();
     wait_vmcnt<0>();
     barrier_no_fence();
@@ -484,7 +506,7 @@ __device__ __forceinline__ void gemm_mainloop2(f32x16 (&acc)[BN / 64][BM / 64], 
     wa = wb;
     xa = xb;
   }
-  stage_head2<BN, BM, false>(acc, f0, f1, wa, xa, px, xf, 0, wn, wm, wv, lane);
+  stage_head2<BN, BM, BM, false>(acc, f0, f1, wa, xa, px, xf, 0, wn, wm, wv, lane);
   mfma_step<BN, BM>(acc, f1);
 }
 
@@ -493,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
     int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
   using C = Cfg2<BN, BM>;
-  __shared__ __attribute__((aligned(1024))) char lds[C::LDS];
+  __shared__ __attribute__((aligned(1024))) char lds[wide_lds_bytes<BN, BM, false>()];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wv >> 1, wm = wv & 1;
@@ -501,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int n0 = tn * BN, m0 = tm * BM;
   f32x16 acc[C::FN][C::FM];
-  gemm_mainloop2<BN, BM>(acc, lds, x, w, M, N, K / BK2, ldx, ldw, m0, n0, wv, lane, K);
+  gemm_mainloop2<BN, BM, false>(acc, lds, x, w, M, N, K / BK2, ldx, ldw, m0, n0, wv, lane, K);
   barrier_no_fence();  // every wavefront is done reading the stages
   store_tile<BN, BM>(acc, lds, y, M, N, ldy, m0, n0, wn, wm, wv, lane);
 }
@@ -535,7 +557,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_partial_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, float *__restrict__ ws,
     int M, int N, int kc, int64_t ldx, int64_t ldw, int tiles_m, int tiles_n) {
   using C = Cfg<BN, BM>;
-  constexpr int LDS_BYTES = WIDE ? Cfg2<BN, BM>::LDS : kStages * C::STAGE;
+  constexpr int LDS_BYTES = WIDE ? wide_lds_bytes<BN, BM, true>() : kStages * C::STAGE;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -548,8 +570,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_partial_kernel(
 
   f32x16 acc[C::FN][C::FM];
   if constexpr (WIDE)
-    gemm_mainloop2<BN, BM>(acc, lds, x + (int64_t)s * kc, w + (int64_t)s * kc, M, N, kc / BK2, ldx,
-                           ldw, m0, n0, wv, lane, kc);
+    gemm_mainloop2<BN, BM, true>(acc, lds, x + (int64_t)s * kc, w + (int64_t)s * kc, M, N,
+                                 kc / BK2, ldx, ldw, m0, n0, wv, lane, kc);
   else
     gemm_mainloop<BN, BM>(acc, lds, x + (int64_t)s * kc, w + (int64_t)s * kc, M, N, kc / BK, ldx,
                           ldw, m0, n0, wv, lane, kc);
