@@ -48,7 +48,8 @@ def parse():
     ap.add_argument("--sweep", default=None)
     ap.add_argument("--only", default=None,
                     choices=["gemm", "gemm_kv", "gemm_up", "gemm_down", "rmsnorm", "shrink_det8",
-                             "shrink_two_pass", "shrink_atomic8", "shrink_unsplit", "copy"])
+                             "shrink_two_pass", "shrink_atomic8", "shrink_unsplit", "copy",
+                             "splitk"])
     ap.add_argument("--iters", type=int, default=50, help="launches for --only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle", type=float, default=0.5,
@@ -477,9 +478,22 @@ def run_only(args, bi, torch, dev, X, G, H, Wq, Wkv, Wup, Wdown, U, A, L, WS, La
     KV = torch.empty((H.shape[0], Wkv.shape[0]), dtype=torch.bfloat16, device=dev)
     U2 = torch.empty_like(U)
     D = torch.empty((H.shape[0], Wdown.shape[0]), dtype=torch.bfloat16, device=dev)
+    # skinny GEMMs: the fixed split-K path on the four projections at M <= 64
+    # (the weight read dominates), each with its split from (N, K)
+    sk = []
+    if args.only == "splitk":
+        ms = min(H.shape[0], 64)
+        for w, inp, y in ((Wq, H, Q), (Wkv, H, KV), (Wup, H, U2), (Wdown, U, D)):
+            S = bi.bi_gemm_splitk_for(w.shape[0], w.shape[1])
+            ws = torch.empty(bi.bi_gemm_splitk_workspace_bytes(ms, w.shape[0], S),
+                             dtype=torch.uint8, device=dev)
+            sk.append((inp[:ms], w, y[:ms], S, ws))
     torch.cuda.synchronize()
     for _ in range(n):
-        if args.only == "gemm":
+        if args.only == "splitk":
+            for inp, w, y, S, ws in sk:
+                bi.bi_gemm_splitk(inp, w, y=y, split_k=S, ws=ws)
+        elif args.only == "gemm":
             bi.bi_gemm(H, Wq, y=Q)
         elif args.only == "gemm_kv":
             bi.bi_gemm(H, Wkv, y=KV)

@@ -607,9 +607,25 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_combine_kernel(
   const int64_t m = e / N, n = e % N;
   f32x4 a = *reinterpret_cast<const f32x4 *>(ws + e);
   f32x4 b = *reinterpret_cast<const f32x4 *>(ws + e + 4);
-  for (int s = 1; s < S; ++s) {
-    a = a + *reinterpret_cast<const f32x4 *>(ws + (int64_t)s * total + e);
-    b = b + *reinterpret_cast<const f32x4 *>(ws + (int64_t)s * total + e + 4);
+  // Partials 1 .. S-1 in groups of 8: a group's loads are all issued before
+  // its adds, which still run in s order (one memory round trip per group,
+  // not per partial).
+  for (int s0 = 1; s0 < S; s0 += 8) {
+    f32x4 pa[8], pb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (s0 + i < S) {
+        pa[i] = *reinterpret_cast<const f32x4 *>(ws + (int64_t)(s0 + i) * total + e);
+        pb[i] = *reinterpret_cast<const f32x4 *>(ws + (int64_t)(s0 + i) * total + e + 4);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (s0 + i < S) {
+        a = a + pa[i];
+        b = b + pb[i];
+      }
+    }
   }
   u32x4 o;
   o[0] = pack_bf16x2(a[0], a[1]);
