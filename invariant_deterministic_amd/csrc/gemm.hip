@@ -17,12 +17,13 @@
 // Data path per workgroup (4 wavefronts, 2 x 2 over the tile):
 //   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS
 //          --ds_read_b128--> VGPR fragments --MFMA--> fp32 accumulators
-//   epilogue: accumulators -> bf16 (round to nearest even) -> 8-byte stores.
+//   epilogue: accumulators -> bf16 (round to nearest even) -> LDS -> whole
+//   128-byte line stores.
 // Two LDS staging schemes feed the same instruction sequence:
-//   * BK = 32 stages (any K % 32 == 0): 64-byte LDS rows, a ring of 4 stages;
-//   * BK = 64 stages (every tile shape, when K % 64 == 0): whole 128-byte
-//     lines per row, so every L2 request is a full line; weights in a ring of
-//     2 stages and activations in a ring of 3 (160 KiB of LDS at 256 x 256).
+//   * BK = 32 stages (K % 64 == 32): 64-byte LDS rows, a ring of 4 stages;
+//   * BK = 64 stages (K % 64 == 0): whole 128-byte lines per row, so every L2
+//     request is a full line; one operand in a ring of 3 stages, the other in
+//     a ring of 2 (160 KiB of LDS at 256 x 256).
 // Each LDS row's 16-byte chunks are XOR-permuted by a function of the row so
 // that the 32 rows a fragment read touches spread over all LDS banks.  Rows
 // beyond M (or N) are loaded as copies of the last valid row and never
@@ -87,25 +88,27 @@ template <int ROWS>
 struct LoadPlan {
   static constexpr int N = ROWS / 64;
   __amdgpu_buffer_rsrc_t rsrc;
-  int off[N];  // byte offsets of this lane's 16-byte pieces, relative to the matrix base
+  // Byte offsets of this lane's 16-byte pieces, relative to the matrix base.
+  // The hardware reads offsets and the record count as unsigned 32-bit
+  // values; the host accepts operands of fewer than 2^31 elements (2^32 bytes).
+  uint32_t off[N];
   __device__ __forceinline__ void init(const uint16_t *g, int rows_total, int row0, int row_limit,
                                        int64_t ld, int K, int wv, int lane) {
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)g, (short)0,
-                                             (int)(((int64_t)(rows_total - 1) * ld + K) * 2),
-                                             0x00020000);
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)g, (short)0, (int)(uint32_t)(((int64_t)(rows_total - 1) * ld + K) * 2), 0x00020000);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int r = i * 64 + wv * 16 + (lane >> 2);
       int gr = row0 + r;
       gr = gr < row_limit ? gr : row_limit - 1;
-      off[i] = ((int)(gr * ld) + (((lane & 3) ^ swz(r)) << 3)) * 2;
+      off[i] = (uint32_t)(gr * ld + (((lane & 3) ^ swz(r)) << 3)) * 2u;
     }
   }
   __device__ __forceinline__ void issue(char *lds, int k0, int wv) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       lds_void *dst = (lds_void *)(lds + (i * 64 + wv * 16) * kRowBytes);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, off[i], k0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, (int)off[i], k0 * 2, 0, 0);
     }
   }
 };
@@ -335,18 +338,17 @@ template <int ROWS>
 struct LoadPlan2 {
   static constexpr int N = ROWS / 32;
   __amdgpu_buffer_rsrc_t rsrc;
-  int off[N];
+  uint32_t off[N];  // as in LoadPlan: unsigned 32-bit byte offsets
   __device__ __forceinline__ void init(const uint16_t *g, int rows_total, int row0, int row_limit,
                                        int64_t ld, int K, int wv, int lane) {
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)g, (short)0,
-                                             (int)(((int64_t)(rows_total - 1) * ld + K) * 2),
-                                             0x00020000);
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)g, (short)0, (int)(uint32_t)(((int64_t)(rows_total - 1) * ld + K) * 2), 0x00020000);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int r = i * 32 + wv * 8 + (lane >> 3);
       int gr = row0 + r;
       gr = gr < row_limit ? gr : row_limit - 1;
-      off[i] = ((int)(gr * ld) + (((lane & 7) ^ swz2(r)) << 3)) * 2;
+      off[i] = (uint32_t)(gr * ld + (((lane & 7) ^ swz2(r)) << 3)) * 2u;
     }
   }
   // instructions [i0, i1) of a stage (compile-time bounds after inlining)
@@ -355,7 +357,7 @@ struct LoadPlan2 {
     for (int i = 0; i < N; ++i) {
       if (i < i0 || i >= i1) continue;
       lds_void *dst = (lds_void *)(lds + (i * 32 + wv * 8) * kRow2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, off[i], k0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, (int)off[i], k0 * 2, 0, 0);
     }
   }
 };
