@@ -6,8 +6,10 @@ with torch's own float32 -> bfloat16 cast (round to nearest, ties to even),
 so that the oracle and the HIP path receive the very same bits.
 
 Distributions follow the workloads the pages talk about (LLM activations and
-weights); none of the pages' datasets is reproduced.  All generators use numpy's
-PCG64 with an explicit seed.
+weights); none of the pages' datasets is reproduced.  Host generators use
+numpy's PCG64 with an explicit seed; inputs of a GiB or more are drawn on the
+device with torch's seeded generator (``device_normal_bf16``), and whatever
+checks them on the host copies back the slices it needs.
 """
 from __future__ import annotations
 
@@ -30,6 +32,16 @@ def normal_bf16(shape, seed: int, mean: float = 0.0, std: float = 1.0) -> np.nda
     g = rng(seed)
     v = g.standard_normal(size=shape) * std + mean
     return f32_to_bf16_bits(v.astype(np.float32))
+
+
+def device_normal_bf16(shape, seed: int, mean: float = 0.0, std: float = 1.0,
+                       device: str = "cuda", dtype=torch.bfloat16) -> torch.Tensor:
+    """N(mean, std^2) samples drawn on the device by torch's seeded generator,
+    cast to ``dtype`` (bf16 by default, round to nearest even)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    t = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    return (t * std + mean).to(dtype)
 
 
 def int_bf16(shape, seed: int, lo: int, hi: int) -> np.ndarray:
