@@ -327,6 +327,19 @@ def sweep(path, bi, torch, dev, to_dev):
                          "config": bi.bi_gemm_config_id(N, K)})
             print(f"# sweep gemm K={K} N={N} M={M}: {recs[-1]['tflops']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
+            cf = bi.bi_gemm_fill_config_id(M, N, K)
+            if cf != bi.bi_gemm_config_id(N, K):
+                # the same bits with the tile picked from M (bi_gemm_fill)
+                if M >= 2048:
+                    msf = _time_loop(torch, lambda i: bi.bi_gemm_fill(xpool[:M], W, y=y), n)
+                else:
+                    msf = _time_loop(torch, lambda i: bi.bi_gemm_fill(xpool[:M], Ws[i % cw], y=y), n)
+                recs.append({"kernel": "bi_gemm_fill", "K": K, "N": N, "M": M, "us": msf * 1e3,
+                             "tflops": fl / (msf * 1e-3) / 1e12,
+                             "frac_mfma": fl / (msf * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                             "config": cf})
+                print(f"# sweep gemm_fill K={K} N={N} M={M} cfg={cf}: "
+                      f"{recs[-1]['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
             if M <= 64:
                 S = bi.bi_gemm_splitk_for(N, K)
                 ws = torch.empty(bi.bi_gemm_splitk_workspace_bytes(M, N, S), dtype=torch.uint8,

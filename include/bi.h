@@ -130,6 +130,31 @@ int bi_gemm_with_config(int config, const uint16_t *x, const uint16_t *w, uint16
                         int64_t ldx, int64_t ldw, int64_t ldy, void *stream);
 
 /*
+ * bi_gemm_fill -- bi_gemm with the tile configuration picked per call from
+ * (M, N, K) to fill the chip, and the same bits as bi_gemm for every input.
+ *
+ * Defined by: "Cómo superar la no determinación en la inferencia de LLM",
+ * section "Multiplicación de matrices (matmul)": the page forces one kernel
+ * configuration because, in the kernels it describes, a different
+ * configuration reduces in a different order.  Here every configuration runs
+ * the same matrix-core instruction over the same ascending k steps (see
+ * bi_gemm_with_config), so the configuration can follow M without any output
+ * bit following it: row i is still bitwise identical alone or in any batch.
+ * The tile is the one with the smallest estimated time: waves of tiles over
+ * the compute units times a measured per-tile cost.  bi_gemm keeps the
+ * single (N, K)-keyed configuration.
+ *
+ * Arguments, layout, ownership and errors as bi_gemm.
+ */
+int bi_gemm_fill(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                 int64_t M, int64_t N, int64_t K,
+                 int64_t ldx, int64_t ldw, int64_t ldy, void *stream);
+
+/* bi_gemm_fill_config_id -- the configuration bi_gemm_fill uses for (M, N, K)
+ * on the current device, or -1 if the shape is not supported (M >= 1). */
+int bi_gemm_fill_config_id(int64_t M, int64_t N, int64_t K);
+
+/*
  * bi_gemm_splitk -- the same product with the K reduction split into split_k
  * equal contiguous chunks, for batches too small to fill the chip with tiles.
  *

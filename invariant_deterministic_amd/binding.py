@@ -42,6 +42,8 @@ _lib_rmsnorm = _sig("bi_rmsnorm", [_p, _p, _p, _i64, _i64, _i64, _i64, ctypes.c_
 _lib_gemm = _sig("bi_gemm", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p])
 _lib_gemm_config_id = _sig("bi_gemm_config_id", [_i64, _i64])
 _lib_gemm_num_configs = _sig("bi_gemm_num_configs", [])
+_lib_gemm_fill = _sig("bi_gemm_fill", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p])
+_lib_gemm_fill_config_id = _sig("bi_gemm_fill_config_id", [_i64, _i64, _i64])
 _lib_gemm_with_config = _sig("bi_gemm_with_config",
                              [_int, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p])
 _lib_gemm_splitk = _sig("bi_gemm_splitk", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _int, _p,
@@ -67,7 +69,8 @@ _lib_row_bitdiff = _sig("bi_row_bitdiff", [_p, _i64, _p, _p, _i64, _p, _i64, _i6
 
 BI_OK = 0
 EXPORTS = ("bi_abi_version", "bi_status_str", "bi_rmsnorm", "bi_gemm", "bi_gemm_config_id",
-           "bi_gemm_num_configs", "bi_gemm_with_config", "bi_gemm_splitk",
+           "bi_gemm_num_configs", "bi_gemm_with_config", "bi_gemm_fill", "bi_gemm_fill_config_id",
+           "bi_gemm_splitk",
            "bi_gemm_splitk_workspace_bytes", "bi_gemm_splitk_for", "bi_gemm_mswitch_control", "bi_lora_shrink_workspace_bytes",
            "bi_lora_shrink", "bi_lora_shrink_two_pass", "bi_lora_shrink_atomic", "bi_row_bitdiff",
            "bi_decode_attention", "bi_decode_attention_workspace_bytes", "bi_lora_expand")
@@ -178,6 +181,26 @@ def bi_gemm_with_config(config: int, x: torch.Tensor, w: torch.Tensor,
     _check(_lib_gemm_with_config(config, px, pw, py, M, N, K, ldx, ldw, ldy, _stream(stream)),
            "bi_gemm_with_config")
     return y
+
+
+def bi_gemm_fill(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """bi_gemm with the tile picked per call to fill the chip; same bits (see bi.h)."""
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    px, ldx = _mat(x, "x", _BF16_LIKE)
+    pw, ldw = _mat(w, "w", _BF16_LIKE)
+    py, ldy = _mat(y, "y", _BF16_LIKE)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y has the wrong shape")
+    _check(_lib_gemm_fill(px, pw, py, M, N, K, ldx, ldw, ldy, _stream(stream)), "bi_gemm_fill")
+    return y
+
+
+def bi_gemm_fill_config_id(M: int, N: int, K: int) -> int:
+    return int(_lib_gemm_fill_config_id(M, N, K))
 
 
 def bi_gemm_splitk_workspace_bytes(M: int, N: int, split_k: int) -> int:

@@ -62,6 +62,15 @@ __device__ __forceinline__ void barrier_no_fence() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Compute units of the current device (256 on MI355X if the query fails).
+inline int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Byte span [lo, hi) touched by a row-major [rows, cols] tensor with stride ld.

@@ -671,6 +671,27 @@ int config_for(int64_t N, int64_t K) {
   return N >= 4096 ? 0 : 2;
 }
 
+// Tile for bi_gemm_fill: the configuration with the smallest estimated time,
+// (waves of tiles over the CUs) x (relative time of one tile).  The tile
+// costs are measured ones, relative to 256 x 256: a 256 x 128 or 128 x 256
+// tile takes ~0.6 of it, a 128 x 128 tile ~0.34.  Ties keep the larger tile.
+int fill_config_for(int64_t M, int64_t N) {
+  static const double kTileCost[kNumConfigs] = {1.0, 0.6, 0.34, 0.58};
+  const int64_t cus = cu_count();
+  int best = 0;
+  double best_t = 0.0;
+  for (int c = 0; c < kNumConfigs; ++c) {
+    const int64_t tiles = ((M + kConfigs[c].bm - 1) / kConfigs[c].bm) *
+                          ((N + kConfigs[c].bn - 1) / kConfigs[c].bn);
+    const double t = (double)((tiles + cus - 1) / cus) * kTileCost[c];
+    if (c == 0 || t < best_t - 1e-9) {
+      best = c;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
 int validate(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t N, int64_t K,
              int64_t ldx, int64_t ldw, int64_t ldy) {
   if (!w || (M > 0 && (!x || !y))) return BI_ERR_NULL;
@@ -719,6 +740,19 @@ extern "C" int bi_gemm(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_
 }
 
 extern "C" int bi_gemm_num_configs(void) { return kNumConfigs; }
+
+extern "C" int bi_gemm_fill_config_id(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 8 || (N & 7) || K < BK || K % BK) return -1;
+  return fill_config_for(M, N);
+}
+
+extern "C" int bi_gemm_fill(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M,
+                            int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
+                            void *stream) {
+  const int st = validate(x, w, y, M, N, K, ldx, ldw, ldy);
+  if (st != BI_OK || M == 0) return st;
+  return launch(fill_config_for(M, N), x, w, y, M, N, K, ldx, ldw, ldy, stream);
+}
 
 extern "C" int bi_gemm_with_config(int config, const uint16_t *x, const uint16_t *w, uint16_t *y,
                                    int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw,

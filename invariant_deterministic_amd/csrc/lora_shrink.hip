@@ -368,14 +368,6 @@ dim3 partial_grid(int64_t M, int S) {
   return dim3((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)S);
 }
 
-int cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
-  return n;
-}
-
 template <int V>
 struct IntC {
   static constexpr int value = V;

@@ -34,7 +34,8 @@ class _Guarded:
     a call must either fail validation or have an empty batch (M == 0)."""
 
     # position of the batch-size argument in each launching entry point
-    M_ARG = {"bi_rmsnorm": 3, "bi_gemm": 3, "bi_gemm_with_config": 4, "bi_lora_shrink": 3,
+    M_ARG = {"bi_rmsnorm": 3, "bi_gemm": 3, "bi_gemm_with_config": 4, "bi_gemm_fill": 3,
+             "bi_lora_shrink": 3,
              "bi_gemm_splitk": 3, "bi_gemm_mswitch_control": 3, "bi_decode_attention": 5, "bi_lora_expand": 4,
              "bi_lora_shrink_two_pass": 3, "bi_lora_shrink_atomic": 3, "bi_row_bitdiff": 6}
 
@@ -67,6 +68,8 @@ def _load():
     L.bi_rmsnorm.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_float, p]
     L.bi_gemm.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, p]
     L.bi_gemm_with_config.argtypes = [i, p, p, p, i64, i64, i64, i64, i64, i64, p]
+    L.bi_gemm_fill.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, p]
+    L.bi_gemm_fill_config_id.argtypes = [i64, i64, i64]
     L.bi_gemm_config_id.argtypes = [i64, i64]
     L.bi_gemm_splitk.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i, p, ctypes.c_size_t, p]
     L.bi_gemm_splitk_workspace_bytes.argtypes = [i64, i64, i]
@@ -149,6 +152,23 @@ def test_gemm_validation(lib):
     assert lib.bi_gemm_with_config(99, X, W, Y, 0, 4096, 4096, 4096, 4096, 4096, None) == \
         BI_ERR_UNSUPPORTED
     assert lib.bi_gemm_with_config(0, X, W, Y, 0, 4096, 4096, 4096, 4096, 4096, None) == BI_OK
+
+
+def test_gemm_fill_validation_and_choice(lib):
+    f = lib.bi_gemm_fill
+    assert f(X, None, Y, 4, 4096, 4096, 4096, 4096, 4096, None) == BI_ERR_NULL
+    assert f(X, W, Y, 4, 4096, 4008, 4008, 4008, 4096, None) == BI_ERR_SHAPE
+    assert f(X, W, Y + 2, 4, 4096, 4096, 4096, 4096, 4096, None) == BI_ERR_ALIGN
+    assert f(X, W, X, 4, 4096, 4096, 4096, 4096, 4096, None) == BI_ERR_ALIAS
+    assert f(X, W, Y, 0, 4096, 4096, 4096, 4096, 4096, None) == BI_OK
+    c = lib.bi_gemm_fill_config_id
+    assert c(0, 4096, 4096) == -1 and c(4, 4100, 4096) == -1 and c(4, 4096, 100) == -1
+    # with 256 CUs (the count assumed when no device answers): the big tile
+    # once it fills the chip, smaller ones below
+    if c(4096, 4096, 4096) == 0:
+        assert c(2048, 4096, 4096) == 3 and c(1000, 4096, 4096) == 2
+        assert c(4096, 14336, 4096) == 0 and c(2048, 14336, 4096) == 0
+        assert c(8192, 1024, 4096) == 3 and c(4096, 1024, 4096) == 2
 
 
 def test_gemm_config_has_no_m_and_is_stable(lib):

@@ -209,3 +209,25 @@ def test_gemm_wide_and_narrow_stages_agree(bi, K):
         wide = host_u16(bi.bi_gemm_with_config(cfg, XP, WP))
         assert np.array_equal(narrow, wide), cfg
     check_bf16(narrow, oracle.gemm(x, w), f"narrow K={K}")
+
+
+def test_gemm_fill_same_bits_as_bi_gemm(bi):
+    """bi_gemm_fill picks its tile from M; every tile runs the same reduction
+    order, so its bits equal bi_gemm's at every M and every projection, and
+    rows stay batch-invariant across the sweep."""
+    from invariant_deterministic_amd import harness
+    c = workloads.LLAMA8B
+    for si, (K, N) in enumerate(c["shapes"]):
+        x = workloads.llama8b_x(K)
+        X = dev_bf16(x)
+        Wt = dev_bf16(workloads.llama8b_w(si))
+        for M in (1, 127, 512, 1000, 2048, 3000, 4096, 8192):
+            say(f"gemm fill K={K} N={N} M={M} cfg={bi.bi_gemm_fill_config_id(M, N, K)}")
+            assert torch.equal(bi.bi_gemm_fill(X[:M], Wt).view(torch.int16),
+                               bi.bi_gemm(X[:M], Wt).view(torch.int16)), (K, N, M)
+        perm = torch.from_numpy(synth.permutation(x.shape[0], c["perm_seed"]))
+        probes = [0, 1, 127, 255, 999, 2047, 4095, 8191]
+        batches = harness.prefix_and_permuted_batches((1, 500, 1000, 2048, 3000, 8192), x.shape[0],
+                                                      perm, "cuda")
+        r = harness.batch_invariance(lambda xb: bi.bi_gemm_fill(xb, Wt), X, probes, batches)
+        assert r["rows"] > 20 and r["diff_bits"] == 0, r
