@@ -304,6 +304,31 @@ size_t bi_decode_attention_workspace_bytes(int64_t B, int64_t H, int64_t Tmax, i
                                            int split_size);
 
 /*
+ * bi_lora_shrink_expand -- the LoRA pair in one launch:
+ *   l = shrink(x, a) as bi_lora_shrink with split_k (fixed-order fold), then
+ *   y = bf16( base + scale * l . b^T ) as bi_lora_expand.
+ *
+ * Defined by: "Reproducible LoRA Inference Through Deterministic Split-K
+ * Reduction", abstract: the two low-rank LoRA multiplications, the shrink with
+ * a deterministic split-K whose fp32 output feeds the expand.
+ *
+ *   x [M, K], a [R, K], b [N, R], base [M, N] (or NULL), y [M, N]: as for
+ *   bi_lora_shrink and bi_lora_expand (same strides, alignment and aliasing
+ *   rules; base may equal y when ldbase == ldy).
+ *   l     optional fp32 [M, R] output (row stride ldl, 16-byte aligned,
+ *         ldl % 4 == 0) receiving the shrink result; NULL to skip it.
+ *   split_k in {1, 2, 4, 8} (BI_ERR_UNSUPPORTED otherwise); K % (32 *
+ *   split_k) == 0.
+ * Order: exactly that of bi_lora_shrink followed by bi_lora_expand, so y (and
+ * l) equal the two-call result bit for bit; l never leaves the chip.
+ */
+int bi_lora_shrink_expand(const uint16_t *x, const uint16_t *a, const uint16_t *b,
+                          const uint16_t *base, uint16_t *y, float *l,
+                          int64_t M, int64_t K, int64_t N, int64_t R,
+                          int64_t ldx, int64_t lda, int64_t ldb, int64_t ldbase, int64_t ldy,
+                          int64_t ldl, float scale, int split_k, void *stream);
+
+/*
  * bi_lora_expand -- LoRA expand: y[m][n] = bf16( base[m][n] + scale * sum_r l[m][r] * b[n][r] ).
  *
  * Defined by: "Reproducible LoRA Inference Through Deterministic Split-K

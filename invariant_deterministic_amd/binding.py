@@ -56,6 +56,9 @@ _lib_attn = _sig("bi_decode_attention", [_p, _p, _p, _p, _p, _i64, _i64, _i64, _
                                          ctypes.c_size_t, _p])
 _lib_attn_ws = _sig("bi_decode_attention_workspace_bytes", [_i64, _i64, _i64, _i64, _int],
                     ctypes.c_size_t)
+_lib_shrink_expand = _sig("bi_lora_shrink_expand",
+                         [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                          _i64, _i64, ctypes.c_float, _int, _p])
 _lib_expand = _sig("bi_lora_expand", [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                       ctypes.c_float, _p])
 _lib_ws_bytes = _sig("bi_lora_shrink_workspace_bytes", [_i64, _i64, _int], ctypes.c_size_t)
@@ -73,7 +76,8 @@ EXPORTS = ("bi_abi_version", "bi_status_str", "bi_rmsnorm", "bi_gemm", "bi_gemm_
            "bi_gemm_splitk",
            "bi_gemm_splitk_workspace_bytes", "bi_gemm_splitk_for", "bi_gemm_mswitch_control", "bi_lora_shrink_workspace_bytes",
            "bi_lora_shrink", "bi_lora_shrink_two_pass", "bi_lora_shrink_atomic", "bi_row_bitdiff",
-           "bi_decode_attention", "bi_decode_attention_workspace_bytes", "bi_lora_expand")
+           "bi_decode_attention", "bi_decode_attention_workspace_bytes", "bi_lora_expand",
+           "bi_lora_shrink_expand")
 
 
 class BiError(RuntimeError):
@@ -378,4 +382,29 @@ def bi_lora_expand(l: torch.Tensor, b: torch.Tensor, base: torch.Tensor | None =
     pbase, ldbase = (None, 0) if base is None else _mat(base, "base", _BF16_LIKE)
     _check(_lib_expand(pl, pb, pbase, py, M, N, R, ldl, ldb, ldbase, ldy, float(scale),
                        _stream(stream)), "bi_lora_expand")
+    return y
+
+
+def bi_lora_shrink_expand(x: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
+                          base: torch.Tensor | None = None, y: torch.Tensor | None = None,
+                          l: torch.Tensor | None = None, scale: float = 1.0, split_k: int = 8,
+                          stream=None) -> torch.Tensor:
+    """y = bf16(base + scale * shrink(x, a) . b^T) in one launch (see bi.h); l, if
+    given (fp32 [M, R]), receives the shrink output."""
+    M, K = x.shape
+    R = a.shape[0]
+    N = b.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    px, ldx = _mat(x, "x", _BF16_LIKE)
+    pa, lda = _mat(a, "a", _BF16_LIKE)
+    pb, ldb = _mat(b, "b", _BF16_LIKE)
+    py, ldy = _mat(y, "y", _BF16_LIKE)
+    pbase, ldbase = _mat(base, "base", _BF16_LIKE) if base is not None else (None, N)
+    pl, ldl = _mat(l, "l", (torch.float32,)) if l is not None else (None, R)
+    if tuple(y.shape) != (M, N) or (base is not None and tuple(base.shape) != (M, N)) or \
+            (l is not None and tuple(l.shape) != (M, R)) or b.shape[1] != R:
+        raise ValueError("shape mismatch")
+    _check(_lib_shrink_expand(px, pa, pb, pbase, py, pl, M, K, N, R, ldx, lda, ldb, ldbase, ldy,
+                              ldl, float(scale), split_k, _stream(stream)), "bi_lora_shrink_expand")
     return y

@@ -314,6 +314,98 @@ __global__ __launch_bounds__(64 * S, 1) void shrink_staged_kernel(
   }
 }
 
+// Fused shrink -> expand: a workgroup of kExpWaves wavefronts per 16-row
+// block.  Wavefronts 0 .. S-1 compute the shrink partials exactly as the
+// streamed fused kernel does (wavefront s: p_s; fold in LDS in s order), so l
+// equals bi_lora_shrink's output bit for bit.  l stays in LDS and all
+// wavefronts expand the block's 16 rows:
+// y[m][n] = bf16(base[m][n] + scale * acc), acc = fma(l[m][r], b[n][r], acc)
+// for r ascending -- the arithmetic of bi_lora_expand, so the result equals
+// expand(shrink(x)) bit for bit.  Each lane owns 4 consecutive columns (b for
+// them widened to fp32 in registers, the 16 rows of base loaded at once); a
+// wavefront covers 256 columns per pass, the workgroup kExpWaves * 256.
+constexpr int kExpWaves = 8;
+template <int S, int STEPS>
+__global__ __launch_bounds__(64 * kExpWaves, 1) void shrink_expand_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
+    const uint16_t *base, uint16_t *y, float *__restrict__ lout, int M, int K, int N,
+    int64_t ldx, int64_t lda, int64_t ldb, int64_t ldbase, int64_t ldy, int64_t ldl, float scale) {
+  static_assert(S <= kExpWaves, "split");
+  const int lane = threadIdx.x & 63;
+  const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m0 = blockIdx.x * kRowsPerWave;
+  __shared__ f32x4 part[S][64];
+  __shared__ float ls[kRowsPerWave][kR];
+  if (s < S) {
+    const int chunk = K / S;
+    const int k0 = s * chunk;
+    int gm = m0 + (lane & 15);
+    gm = gm < M ? gm : M - 1;  // rows past M read a copy of the last row, never stored
+    const int koff = (lane >> 4) * 8;
+    const bf16x8 *xp = reinterpret_cast<const bf16x8 *>(x + (int64_t)gm * ldx + k0 + koff);
+    const bf16x8 *ap = reinterpret_cast<const bf16x8 *>(a + (int64_t)(lane & 15) * lda + k0 + koff);
+    part[s][lane] = chunk_partial<STEPS, 1>(xp, ap, chunk / kStep);
+  }
+  __syncthreads();
+  if (s == 0) {
+    f32x4 t = part[0][lane];
+#pragma unroll
+    for (int q = 1; q < S; ++q) t = t + part[q][lane];  // element-wise fp32, q ascending
+    const int row = lane & 15, r0 = (lane >> 4) * 4;
+    *reinterpret_cast<f32x4 *>(&ls[row][r0]) = t;
+    if (lout != nullptr && m0 + row < M)
+      *reinterpret_cast<f32x4 *>(lout + (int64_t)(m0 + row) * ldl + r0) = t;
+  }
+  __syncthreads();  // l of the block is in LDS
+
+  const int nrows = min(kRowsPerWave, M - m0);
+  for (int nt = 0; nt < N; nt += kExpWaves * 256) {
+    const int n0 = nt + s * 256 + lane * 4;
+    if (n0 >= N) continue;  // N % 8 == 0: a lane's 4 columns are all in or all out
+    u32x2 bv[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int m = m0 + (i < nrows ? i : nrows - 1);
+      bv[i] = base ? __builtin_nontemporal_load(
+                         reinterpret_cast<const u32x2 *>(base + (int64_t)m * ldbase + n0))
+                   : u32x2{0u, 0u};
+    }
+    float bf[4][kR];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 *br = reinterpret_cast<const u32x4 *>(b + (int64_t)(n0 + j) * ldb);
+      const u32x4 w0 = br[0], w1 = br[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bf[j][2 * i] = lo_bf16(w0[i]);
+        bf[j][2 * i + 1] = hi_bf16(w0[i]);
+        bf[j][8 + 2 * i] = lo_bf16(w1[i]);
+        bf[j][8 + 2 * i + 1] = hi_bf16(w1[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      if (i >= nrows) continue;
+      // one row's l at a time: hoisting every row's reads would need 256 registers
+      __builtin_amdgcn_sched_barrier(0);
+      float lv[kR];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) lv[r] = ls[i][r];
+      u32x2 o;
+      float acc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) acc[j] = __builtin_fmaf(lv[r], bf[j][r], acc[j]);
+      }
+      o[0] = pack_bf16x2(lo_bf16(bv[i][0]) + scale * acc[0], hi_bf16(bv[i][0]) + scale * acc[1]);
+      o[1] = pack_bf16x2(lo_bf16(bv[i][1]) + scale * acc[2], hi_bf16(bv[i][1]) + scale * acc[3]);
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x2 *>(y + (int64_t)(m0 + i) * ldy + n0));
+    }
+  }
+}
+
 // Fixed-order combine: y[m][r] = (((p_0 + p_1) + p_2) + ...) + p_{S-1}.
 __global__ __launch_bounds__(kThreads) void shrink_combine_kernel(const float *__restrict__ ws,
                                                                   float *__restrict__ y, int M,
@@ -501,5 +593,53 @@ extern "C" int bi_lora_shrink_atomic(const uint16_t *x, const uint16_t *a, float
                      dim3(kThreads), 0, s, y, (int)M, ldy);
   if ((st = launch_status()) != BI_OK) return st;
   launch_fused<kAtomic>(split_k, s, x, a, y, nullptr, M, K, ldx, lda, ldy);
+  return launch_status();
+}
+
+extern "C" int bi_lora_shrink_expand(const uint16_t *x, const uint16_t *a, const uint16_t *b,
+                                     const uint16_t *base, uint16_t *y, float *l, int64_t M,
+                                     int64_t K, int64_t N, int64_t R, int64_t ldx, int64_t lda,
+                                     int64_t ldb, int64_t ldbase, int64_t ldy, int64_t ldl,
+                                     float scale, int split_k, void *stream) {
+  if (!a || !b || (M > 0 && (!x || !y))) return BI_ERR_NULL;
+  if (R != kR || !split_ok(split_k) || split_k > 8) return BI_ERR_UNSUPPORTED;
+  if (M < 0 || K <= 0 || M > (1 << 30) || K > (1 << 30) || N < 8 || N > (1 << 23) || ldx < K ||
+      lda < K || ldb < R || ldy < N || (base && ldbase < N) || (l && ldl < R))
+    return BI_ERR_SHAPE;
+  if (K % (kStep * split_k)) return BI_ERR_SHAPE;
+  if ((ldx | lda | N | ldy | ldb) & 7 || (base && (ldbase & 7)) || (l && (ldl & 3)) ||
+      !aligned16(x) || !aligned16(a) || !aligned16(b) || !aligned16(y) ||
+      (base && !aligned16(base)) || (l && !aligned16(l)))
+    return BI_ERR_ALIGN;
+  const Span sy = span_of(y, M, N, ldy, 2);
+  const bool in_place = base == y && ldbase == ldy;
+  if (overlap(sy, span_of(x, M, K, ldx, 2)) || overlap(sy, span_of(a, R, K, lda, 2)) ||
+      overlap(sy, span_of(b, N, R, ldb, 2)) ||
+      (base && !in_place && overlap(sy, span_of(base, M, N, ldbase, 2))))
+    return BI_ERR_ALIAS;
+  if (l) {
+    const Span sl = span_of(l, M, R, ldl, 4);
+    if (overlap(sl, sy) || overlap(sl, span_of(x, M, K, ldx, 2)) ||
+        overlap(sl, span_of(a, R, K, lda, 2)) || overlap(sl, span_of(b, N, R, ldb, 2)) ||
+        (base && overlap(sl, span_of(base, M, N, ldbase, 2))))
+      return BI_ERR_ALIAS;
+  }
+  if (M == 0) return BI_OK;
+  const dim3 grid((unsigned)((M + kRowsPerWave - 1) / kRowsPerWave));
+  hipStream_t st = (hipStream_t)stream;
+  with_steps((int)(K / split_k / kStep), [&](auto c) {
+    constexpr int ST = decltype(c)::value;
+    auto go = [&](auto sc) {
+      constexpr int SS = decltype(sc)::value;
+      hipLaunchKernelGGL((shrink_expand_kernel<SS, ST>), grid, dim3(64 * kExpWaves), 0, st, x, a, b, base,
+                         y, l, (int)M, (int)K, (int)N, ldx, lda, ldb, ldbase, ldy, ldl, scale);
+    };
+    switch (split_k) {
+      case 1: go(IntC<1>{}); break;
+      case 2: go(IntC<2>{}); break;
+      case 4: go(IntC<4>{}); break;
+      default: go(IntC<8>{}); break;
+    }
+  });
   return launch_status();
 }

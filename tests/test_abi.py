@@ -36,7 +36,7 @@ class _Guarded:
     # position of the batch-size argument in each launching entry point
     M_ARG = {"bi_rmsnorm": 3, "bi_gemm": 3, "bi_gemm_with_config": 4, "bi_gemm_fill": 3,
              "bi_lora_shrink": 3,
-             "bi_gemm_splitk": 3, "bi_gemm_mswitch_control": 3, "bi_decode_attention": 5, "bi_lora_expand": 4,
+             "bi_gemm_splitk": 3, "bi_gemm_mswitch_control": 3, "bi_decode_attention": 5, "bi_lora_expand": 4, "bi_lora_shrink_expand": 6,
              "bi_lora_shrink_two_pass": 3, "bi_lora_shrink_atomic": 3, "bi_row_bitdiff": 6}
 
     def __init__(self, lib):
@@ -86,6 +86,8 @@ def _load():
     L.bi_decode_attention_workspace_bytes.argtypes = [i64, i64, i64, i64, i]
     L.bi_decode_attention_workspace_bytes.restype = ctypes.c_size_t
     L.bi_lora_expand.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i64, ctypes.c_float, p]
+    L.bi_lora_shrink_expand.argtypes = [p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, i64, i64,
+                                        i64, ctypes.c_float, i, p]
     L.bi_status_str.restype = ctypes.c_char_p
     return L
 
@@ -267,3 +269,25 @@ def test_lora_expand_validation(lib):
     assert f(X, W, Y + 16, Y, 4, 4096, 16, 16, 16, 4096, 4096, 1.0, None) == BI_ERR_ALIAS
     assert f(X, W, None, X, 4, 4096, 16, 16, 16, 0, 4096, 1.0, None) == BI_ERR_ALIAS
     assert f(None, W, None, None, 0, 4096, 16, 16, 16, 0, 4096, 1.0, None) == BI_OK
+
+
+def test_shrink_expand_validation(lib):
+    f = lib.bi_lora_shrink_expand
+    B, BASE, L = 0x50000000, 0x60000000, 0x70000000
+    ok = (4096, 4096, 4096, 16, 4096, 4096, 16, 4096, 4096, 16)   # M K N R ldx lda ldb ldbase ldy ldl
+    assert f(X, W, None, BASE, Y, L, *ok, 1.0, 8, None) == BI_ERR_NULL
+    assert f(X, W, B, BASE, Y, L, 4096, 4096, 4096, 8, 4096, 4096, 16, 4096, 4096, 16, 1.0, 8,
+             None) == BI_ERR_UNSUPPORTED                                            # R != 16
+    assert f(X, W, B, BASE, Y, L, *ok, 1.0, 16, None) == BI_ERR_UNSUPPORTED          # split 16
+    assert f(X, W, B, BASE, Y, L, *ok, 1.0, 3, None) == BI_ERR_UNSUPPORTED
+    assert f(X, W, B, BASE, Y, L, 4096, 4064, 4096, 16, 4096, 4096, 16, 4096, 4096, 16, 1.0, 8,
+             None) == BI_ERR_SHAPE                                                  # K % 256
+    assert f(X, W, B, BASE, Y, L, 4096, 4096, 4100, 16, 4096, 4096, 16, 4100, 4100, 16, 1.0, 8,
+             None) == BI_ERR_ALIGN                                                  # N % 8
+    assert f(X, W, B, BASE, Y, L + 4, *ok, 1.0, 8, None) == BI_ERR_ALIGN
+    assert f(X, W, B, BASE, X, L, *ok, 1.0, 8, None) == BI_ERR_ALIAS                 # y over x
+    assert f(X, W, B, BASE, Y, Y, *ok, 1.0, 8, None) == BI_ERR_ALIAS                 # l over y
+    assert f(X, W, B, Y, Y, L, 0, *ok[1:], 1.0, 8, None) == BI_OK                   # in place
+    assert f(X, W, B, Y + 64, Y, L, 4096, *ok[1:], 1.0, 8, None) == BI_ERR_ALIAS     # base shifted onto y
+    assert f(None, W, B, None, None, None, 0, 4096, 4096, 16, 4096, 4096, 16, 4096, 4096, 16, 1.0,
+             8, None) == BI_OK

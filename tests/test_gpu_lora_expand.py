@@ -78,3 +78,41 @@ def test_shrink_then_expand_end_to_end(bi):
     for i in (0, 100, 256):
         assert np.array_equal(run([i])[0], full[i])
     say("shrink -> expand: parity and single-row invariance ok")
+
+
+@pytest.mark.parametrize("split", [1, 2, 4, 8])
+def test_shrink_expand_fused_equals_two_calls(bi, split):
+    """One launch gives the bits of bi_lora_shrink followed by bi_lora_expand
+    (y and the optional l), with and without base, at ragged M and N."""
+    K = 4096
+    a = dev_bf16(synth.normal_bf16((16, K), 941, std=0.01))
+    for M, N in ((1, 8), (17, 520), (300, 4096), (1000, 5000)):
+        say(f"shrink_expand split={split} M={M} N={N}")
+        x = dev_bf16(synth.normal_bf16((M, K), 942 + M))
+        b = dev_bf16(synth.normal_bf16((N, 16), 943 + N, std=0.02))
+        base = dev_bf16(synth.normal_bf16((M, N), 944 + M))
+        for bs, scale in ((base, 0.5), (None, 2.0)):
+            l_ref = bi.bi_lora_shrink(x, a, split_k=split)
+            y_ref = bi.bi_lora_expand(l_ref, b, base=bs, scale=scale)
+            l = torch.empty_like(l_ref)
+            y = bi.bi_lora_shrink_expand(x, a, b, base=bs, l=l, scale=scale, split_k=split)
+            assert torch.equal(l.view(torch.int32), l_ref.view(torch.int32)), (M, N)
+            assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (M, N, bs is None)
+
+
+def test_shrink_expand_parity_invariance_and_in_place(bi):
+    M, K, N = 300, 4096, 4096
+    x = synth.normal_bf16((M, K), 951)
+    a = synth.normal_bf16((16, K), 952, std=0.01)
+    b = synth.normal_bf16((N, 16), 953, std=0.02)
+    base = synth.normal_bf16((M, N), 954)
+    X, A, B, BASE = dev_bf16(x), dev_bf16(a), dev_bf16(b), dev_bf16(base)
+    y = host_u16(bi.bi_lora_shrink_expand(X, A, B, base=BASE, scale=0.5))
+    l64 = oracle.lora_shrink(x, a)
+    check_bf16(y, oracle.lora_expand(l64.astype(np.float32), b, base, scale=0.5), "shrink_expand")
+    for r in (0, 1, 15, 16, 299):
+        solo = host_u16(bi.bi_lora_shrink_expand(X[r:r + 1], A, B, base=BASE[r:r + 1], scale=0.5))
+        assert np.array_equal(solo[0], y[r]), r
+    inplace = BASE.clone()
+    bi.bi_lora_shrink_expand(X, A, B, base=inplace, y=inplace, scale=0.5)
+    assert np.array_equal(host_u16(inplace), y)
