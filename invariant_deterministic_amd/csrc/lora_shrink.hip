@@ -300,7 +300,8 @@ __global__ __launch_bounds__(64 * S, 1) void shrink_staged_kernel(
     const int m0 = ((int)blockIdx.x + bi * (int)gridDim.x) * kRowsPerWave;
     emit<S, MODE>(acc, part[bi & 1], y, ws, M, ldy, m0, s, lane);
   }
-  {  // last block: pieces npieces - NP .. npieces - 1, nothing more to issue
+  {  // last block: pieces npieces - NP .. npieces - 1; the first two are in
+     // flight already, each later one is issued two pieces ahead (NP > 2)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
@@ -308,6 +309,8 @@ __global__ __launch_bounds__(64 * S, 1) void shrink_staged_kernel(
       if (p + 1 < NP) wait_vmcnt<NI>();
       else wait_vmcnt<0>();
       compute(j, p, acc);
+      if (p + 2 < NP) issue(j + 2);
+      __builtin_amdgcn_sched_barrier(0);
     }
     const int m0 = ((int)blockIdx.x + bi * (int)gridDim.x) * kRowsPerWave;
     emit<S, MODE>(acc, part[bi & 1], y, ws, M, ldy, m0, s, lane);

@@ -33,7 +33,8 @@ def _run(bi, q, k, v, lens, split):
 
 
 @pytest.mark.parametrize("H,Hkv,D,split", [(32, 8, 128, 256), (8, 8, 64, 128), (16, 2, 128, 512),
-                                           (4, 1, 64, 256)])
+                                           (4, 1, 64, 256), (8, 4, 128, 128), (6, 2, 64, 512),
+                                           (14, 2, 128, 256)])
 def test_attention_parity(bi, H, Hkv, D, split):
     B, Tmax = 5, 1100
     q, k, v = _inputs(B, H, Hkv, D, Tmax, 700 + H)

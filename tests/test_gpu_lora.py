@@ -192,3 +192,24 @@ def test_shrink_strided_output(bi):
     o = host_f32(out)
     check_f32(o[:, :16], oracle.lora_shrink(x, a), "strided atomic")
     assert np.all(o[:, 16:] == 7.0)
+
+
+@pytest.mark.parametrize("K", [512, 1024, 2048, 8192, 14336])
+def test_shrink_other_k_every_path(bi, K):
+    """K other than 4096 reaches the other kernels: the staged kernel only at 16
+    (S = 8) or 8/16 (S = 16) steps a chunk; the streamed kernel at the other
+    compiled step counts (8, 32, 64, 128); the one-step-at-a-time loop at run-time
+    counts (K = 14336: 56 steps a chunk at S = 8).  Exact integer inputs, every
+    split that divides K, the three variants."""
+    for split in (1, 2, 4, 8, 16):
+        if K % (32 * split):
+            continue
+        for M in (1, 33):
+            x = synth.int_bf16((M, K), K + M, -4, 4)
+            a = synth.int_bf16((16, K), K + M + 1, -4, 4)
+            want = oracle.lora_shrink(x, a).astype(np.float32)
+            X, A = dev_bf16(x), dev_bf16(a)
+            say(f"shrink K={K} split={split} M={M}")
+            assert np.array_equal(host_f32(bi.bi_lora_shrink(X, A, split_k=split)), want), split
+            assert np.array_equal(host_f32(bi.bi_lora_shrink_two_pass(X, A, split_k=split)), want)
+            assert np.array_equal(host_f32(bi.bi_lora_shrink_atomic(X, A, split_k=split)), want)
