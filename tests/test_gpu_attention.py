@@ -94,3 +94,12 @@ def test_attention_split_sizes_agree_within_tolerance(bi):
     ref = oracle.decode_attention(q, k, v, lens)
     for split in (128, 256, 512):
         check_bf16(_run(bi, q, k, v, lens, split), ref, f"split {split}")
+
+
+def test_attention_lengths_outside_range_are_clamped(bi):
+    """lens below 1 act as 1 and above Tmax as Tmax (as the header says)."""
+    B, H, Hkv, D, Tmax = 3, 8, 2, 64, 300
+    q, k, v = _inputs(B, H, Hkv, D, Tmax, 760)
+    o = _run(bi, q, k, v, [0, Tmax + 7, -5], 128)
+    want = _run(bi, q, k, v, [1, Tmax, 1], 128)
+    assert np.array_equal(o, want)

@@ -213,3 +213,18 @@ def test_shrink_other_k_every_path(bi, K):
             assert np.array_equal(host_f32(bi.bi_lora_shrink(X, A, split_k=split)), want), split
             assert np.array_equal(host_f32(bi.bi_lora_shrink_two_pass(X, A, split_k=split)), want)
             assert np.array_equal(host_f32(bi.bi_lora_shrink_atomic(X, A, split_k=split)), want)
+
+
+@pytest.mark.parametrize("K,split", [(4096, 8), (4096, 16), (8192, 16)])
+def test_shrink_staged_persistent_blocks(bi, K, split):
+    """The staged kernel is persistent: with more 16-row blocks than
+    workgroups each workgroup runs several blocks, its loads running one block
+    ahead.  M = 8209 gives 514 blocks (two or three per workgroup on 256 CUs)
+    and a ragged last block; exact integer inputs."""
+    M = 8209
+    x = synth.int_bf16((M, K), K + split, -4, 4)
+    a = synth.int_bf16((16, K), K + split + 1, -4, 4)
+    want = oracle.lora_shrink(x, a).astype(np.float32)
+    X, A = dev_bf16(x), dev_bf16(a)
+    say(f"shrink staged K={K} split={split} M={M}")
+    assert np.array_equal(host_f32(bi.bi_lora_shrink(X, A, split_k=split)), want)
