@@ -45,7 +45,7 @@ def _pin_inputs(name, rows=5, n=16, col=3):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1024, 1024), (37, 520, 4096), (64, 4096, 4096),
-                                   (130, 264, 14336), (37, 520, 2112)])
+                                   (130, 264, 14336), (37, 520, 2112), (5, 264, 2048)])
 def test_splitk_integer_inputs_bitwise(bi, M, N, K):
     """Exact in every order.  Chunks of K / S with K / S % 64 == 0 run 64-k
     LDS stages, the others 32-k stages (K = 2112: S = 1 and S = 2 take one
@@ -54,7 +54,7 @@ def test_splitk_integer_inputs_bitwise(bi, M, N, K):
     w = synth.int_bf16((N, K), N + 7, -4, 4)
     want = oracle.bf16_round(oracle.gemm(x, w))
     X, Wt = dev_bf16(x), dev_bf16(w)
-    for S in (1, 2, 4, 8):
+    for S in (1, 2, 4, 8, 16, 32, 64):
         if K % (32 * S):
             continue
         say(f"splitk int M={M} N={N} K={K} S={S}")
