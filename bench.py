@@ -64,7 +64,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
               "this path has no multi-GPU mode; row sharding needs no exchange and is "
-              "described in DESIGN.md", file=sys.stderr)
+              "written up with the design notes", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -52,7 +52,7 @@ typedef enum bi_status {
     BI_ERR_WORKSPACE = 4,   /* split-K workspace missing or too small             */
     BI_ERR_ALIAS = 5,       /* an output overlaps an input or another output      */
     BI_ERR_HIP = 6,         /* the HIP runtime reported an error at launch        */
-    BI_ERR_UNSUPPORTED = 7  /* valid request this build does not implement        */
+    BI_ERR_UNSUPPORTED = 7  /* valid request the library does not implement      */
 } bi_status;
 
 /* BI_ABI_VERSION of the loaded library. */

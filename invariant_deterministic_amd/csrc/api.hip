@@ -12,7 +12,7 @@ extern "C" const char *bi_status_str(int status) {
     case BI_ERR_WORKSPACE: return "BI_ERR_WORKSPACE: split-K workspace missing or too small";
     case BI_ERR_ALIAS: return "BI_ERR_ALIAS: an output overlaps another tensor";
     case BI_ERR_HIP: return "BI_ERR_HIP: the HIP runtime reported an error";
-    case BI_ERR_UNSUPPORTED: return "BI_ERR_UNSUPPORTED: not implemented in this build";
+    case BI_ERR_UNSUPPORTED: return "BI_ERR_UNSUPPORTED: not implemented by the library";
     default: return "unknown bi_status";
   }
 }
