@@ -1,0 +1,96 @@
+"""The entry points launch on the caller's stream and allocate nothing, so a
+chain of them can run on a side stream and be captured in a HIP graph.  Every
+replay (with eager work in between) must reproduce the eager bits."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from invariant_deterministic_amd import synth, workloads
+from tests.gpu_util import dev_bf16, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bi():
+    need_gpu()
+    from invariant_deterministic_amd import binding
+    return binding
+
+
+def _inputs():
+    M, K, N = 300, 4096, 1024
+    X = dev_bf16(synth.normal_bf16((M, K), 9001))
+    G = dev_bf16(synth.normal_bf16((K,), 9002, mean=1.0, std=0.1))
+    W = dev_bf16(synth.normal_bf16((N, K), 9003, std=0.02))
+    A = dev_bf16(synth.normal_bf16((16, K), 9004, std=0.01))
+    B = dev_bf16(synth.normal_bf16((N, 16), 9005, std=0.02))
+    return X, G, W, A, B
+
+
+def _chain(bi, X, G, W, A, B, H, Y, L, Z, Ya):
+    bi.bi_rmsnorm(X, G, y=H, eps=workloads.EPS)
+    bi.bi_gemm(H, W, y=Y)
+    bi.bi_lora_shrink(H, A, y=L, split_k=8)
+    bi.bi_lora_expand(L, B, base=Y, y=Z, scale=0.5)
+    bi.bi_lora_shrink_atomic(H, A, y=Ya, split_k=8)
+
+
+def _buffers(X, W):
+    M, N = X.shape[0], W.shape[0]
+    dev = X.device
+    return (torch.empty_like(X), torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+            torch.empty((M, 16), dtype=torch.float32, device=dev),
+            torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+            torch.empty((M, 16), dtype=torch.float32, device=dev))
+
+
+def test_side_stream_matches_default_stream(bi):
+    X, G, W, A, B = _inputs()
+    ref = _buffers(X, W)
+    _chain(bi, X, G, W, A, B, *ref)
+    torch.cuda.synchronize()
+    out = _buffers(X, W)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _chain(bi, X, G, W, A, B, *out)
+    s.synchronize()
+    for r, o in list(zip(ref, out))[:4]:
+        assert torch.equal(r.view(torch.int16) if r.dtype == torch.bfloat16 else r.view(torch.int32),
+                           o.view(torch.int16) if o.dtype == torch.bfloat16 else o.view(torch.int32))
+    assert torch.allclose(ref[4], out[4], rtol=1e-5, atol=1e-5)   # the atomic control: values only
+
+
+def test_graph_replays_reproduce_eager_bits(bi):
+    X, G, W, A, B = _inputs()
+    ref = _buffers(X, W)
+    _chain(bi, X, G, W, A, B, *ref)
+    torch.cuda.synchronize()
+    out = _buffers(X, W)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _chain(bi, X, G, W, A, B, *out)          # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _chain(bi, X, G, W, A, B, *out)
+    for rep in range(3):
+        for t in out:
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"graph replay {rep}")
+        for r, o in list(zip(ref, out))[:4]:
+            if r.dtype == torch.bfloat16:
+                assert torch.equal(r.view(torch.int16), o.view(torch.int16)), rep
+            else:
+                assert torch.equal(r.view(torch.int32), o.view(torch.int32)), rep
+        assert torch.allclose(ref[4], out[4], rtol=1e-5, atol=1e-5), rep
+        _chain(bi, X, G, W, A, B, *_buffers(X, W))   # eager work between replays
+        torch.cuda.synchronize()
