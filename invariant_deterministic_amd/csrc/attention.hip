@@ -240,11 +240,20 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float *__restrict
   const float *p = ws + ((int64_t)b * H + h) * nc_max * (D + 2);
   constexpr int S = D + 2;  // floats per chunk record
 
+  // The first tile's loads (its statistics and values) do not depend on M:
+  // they go out together with the loads M needs, so the usual case (at most
+  // kCT chunks) costs one memory round trip after the length.
+  float a[kCT];
+#pragma unroll
+  for (int i = 0; i < kCT; ++i) a[i] = i < nc ? p[(int64_t)i * S + d] : 0.0f;
+  const float m_own = d < nc ? p[(int64_t)d * S + D] : -INFINITY;
+  const float l_own = d < nc ? p[(int64_t)d * S + D + 1] : 0.0f;
+
   // M: every thread takes the max over its chunks, then a max over threads
   // (max is exact, so the grouping does not matter).
   __shared__ float red[D / 64];
-  float m = -INFINITY;
-  for (int c = d; c < nc; c += D) m = fmaxf(m, p[(int64_t)c * S + D]);
+  float m = m_own;
+  for (int c = d + D; c < nc; c += D) m = fmaxf(m, p[(int64_t)c * S + D]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   if ((d & 63) == 0) red[d >> 6] = m;
@@ -259,12 +268,18 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float *__restrict
     const int n = min(kCT, nc - c0);
     __syncthreads();  // the previous tile's fw / lw are consumed
     if (d < n) {
-      fw[d] = expf(p[(int64_t)(c0 + d) * S + D] - M);
-      lw[d] = p[(int64_t)(c0 + d) * S + D + 1];
+      if (c0 == 0) {
+        fw[d] = expf(m_own - M);
+        lw[d] = l_own;
+      } else {
+        fw[d] = expf(p[(int64_t)(c0 + d) * S + D] - M);
+        lw[d] = p[(int64_t)(c0 + d) * S + D + 1];
+      }
     }
-    float a[kCT];
+    if (c0 > 0) {
 #pragma unroll
-    for (int i = 0; i < kCT; ++i) a[i] = i < n ? p[(int64_t)(c0 + i) * S + d] : 0.0f;
+      for (int i = 0; i < kCT; ++i) a[i] = i < n ? p[(int64_t)(c0 + i) * S + d] : 0.0f;
+    }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kCT; ++i) {
