@@ -141,8 +141,12 @@ int bi_gemm_with_config(int config, const uint16_t *x, const uint16_t *w, uint16
  * bi_gemm_with_config), so the configuration can follow M without any output
  * bit following it: row i is still bitwise identical alone or in any batch.
  * The tile is the one with the smallest estimated time: waves of tiles over
- * the compute units times a measured per-tile cost.  bi_gemm keeps the
- * single (N, K)-keyed configuration.
+ * the compute units times a measured per-tile cost.  One more launch is
+ * considered when K % 64 == 0 and the 256 x 256 tiles make one or two whole
+ * waves and a last one at most half full: that last wave is cut into
+ * 256 x 128 halves, so that it occupies twice the compute units for about
+ * 0.6 of a tile's time.  bi_gemm keeps the single
+ * (N, K)-keyed configuration.
  *
  * Arguments, layout, ownership and errors as bi_gemm.
  */
@@ -151,7 +155,8 @@ int bi_gemm_fill(const uint16_t *x, const uint16_t *w, uint16_t *y,
                  int64_t ldx, int64_t ldw, int64_t ldy, void *stream);
 
 /* bi_gemm_fill_config_id -- the configuration bi_gemm_fill uses for (M, N, K)
- * on the current device, or -1 if the shape is not supported (M >= 1). */
+ * on the current device (bi_gemm_num_configs() for the mixed launch), or -1
+ * if the shape is not supported (M >= 1). */
 int bi_gemm_fill_config_id(int64_t M, int64_t N, int64_t K);
 
 /*

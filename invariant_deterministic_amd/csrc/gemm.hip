@@ -63,11 +63,16 @@ struct Cfg {
 // on one XCD share weight and activation panels in that XCD's L2.  The mapping
 // changes which workgroup computes a tile, never how the tile is computed.
 constexpr int kGroupM = 4;
-__device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int &tm, int &tn) {
-  const int T = tiles_m * tiles_n;
+// Launch index -> logical tile index: each XCD gets a contiguous range of the
+// T logical tiles.
+__device__ __forceinline__ int xcd_lid(int pid, int T) {
   const int q = T >> 3, r = T & 7;
   const int xcd = pid & 7, local = pid >> 3;
-  const int lid = xcd * q + (xcd < r ? xcd : r) + local;
+  return xcd * q + (xcd < r ? xcd : r) + local;
+}
+// Logical tile index -> (tile row, tile column), walking groups of kGroupM
+// tile-rows column by column.
+__device__ __forceinline__ void group_tile(int lid, int tiles_m, int tiles_n, int &tm, int &tn) {
   const int per_group = kGroupM * tiles_n;
   const int g = lid / per_group;
   const int first_m = g * kGroupM;
@@ -75,6 +80,9 @@ __device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int &
   const int in_g = lid - g * per_group;
   tm = first_m + in_g % gsize;
   tn = in_g / gsize;
+}
+__device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int &tm, int &tn) {
+  group_tile(xcd_lid(pid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 // Direct-to-LDS loads of one operand tile through a buffer resource: each lane
@@ -512,22 +520,54 @@ __device__ __forceinline__ void gemm_mainloop2(f32x16 (&acc)[BN / 64][BM / 64], 
   mfma_step<BN, BM>(acc, f1);
 }
 
+// One BN x BM output tile with 64-k stages, at rows m0.., columns n0...
 template <int BN, int BM>
-__global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
-    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+__device__ __forceinline__ void wide_tile(char *lds, const uint16_t *__restrict__ x,
+                                          const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+                                          int M, int N, int K, int64_t ldx, int64_t ldw,
+                                          int64_t ldy, int m0, int n0) {
   using C = Cfg2<BN, BM>;
-  __shared__ __attribute__((aligned(1024))) char lds[wide_lds_bytes<BN, BM, false>()];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wv >> 1, wm = wv & 1;
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int n0 = tn * BN, m0 = tm * BM;
   f32x16 acc[C::FN][C::FM];
   gemm_mainloop2<BN, BM, false>(acc, lds, x, w, M, N, K / BK2, ldx, ldw, m0, n0, wv, lane, K);
   barrier_no_fence();  // every wavefront is done reading the stages
   store_tile<BN, BM>(acc, lds, y, M, N, ldy, m0, n0, wn, wm, wv, lane);
+}
+
+template <int BN, int BM>
+__global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char lds[wide_lds_bytes<BN, BM, false>()];
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  wide_tile<BN, BM>(lds, x, w, y, M, N, K, ldx, ldw, ldy, tm * BM, tn * BN);
+}
+
+// 256 x 256 tiles whose last, partly filled wave is split in two along M: the
+// first nfull launch indices take whole tiles (logical tiles 0 .. nfull-1),
+// the rest take 256 x 128 halves of the remaining logical tiles, two launch
+// indices per tile.  Both shapes run the same matrix-core steps in the same
+// order, so no output's bits depend on which kind of workgroup computed it.
+__global__ __launch_bounds__(kThreads, 1) void gemm_mixed_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n,
+    int nfull) {
+  __shared__ __attribute__((aligned(1024))) char lds[wide_lds_bytes<256, 256, false>()];
+  const int pid = blockIdx.x;
+  int tm, tn;
+  if (pid < nfull) {
+    group_tile(xcd_lid(pid, nfull), tiles_m, tiles_n, tm, tn);
+    wide_tile<256, 256>(lds, x, w, y, M, N, K, ldx, ldw, ldy, tm * 256, tn * 256);
+  } else {
+    const int q = pid - nfull;
+    group_tile(nfull + (q >> 1), tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * 256 + (q & 1) * 128;
+    if (m0 >= M) return;  // the empty lower half of the last tile row
+    wide_tile<256, 128>(lds, x, w, y, M, N, K, ldx, ldw, ldy, m0, tn * 256);
+  }
 }
 
 template <int BN, int BM>
@@ -675,7 +715,10 @@ int config_for(int64_t N, int64_t K) {
 // (waves of tiles over the CUs) x (relative time of one tile).  The tile
 // costs are measured ones, relative to 256 x 256: a 256 x 128 or 128 x 256
 // tile takes ~0.6 of it, a 128 x 128 tile ~0.34.  Ties keep the larger tile.
-int fill_config_for(int64_t M, int64_t N) {
+// kMixed: 256 x 256 tiles with the last wave split into 256 x 128 halves
+// (gemm_mixed_kernel); only for 64-k stages.
+constexpr int kMixed = kNumConfigs;
+int fill_config_for(int64_t M, int64_t N, int64_t K) {
   static const double kTileCost[kNumConfigs] = {1.0, 0.6, 0.34, 0.58};
   const int64_t cus = cu_count();
   int best = 0;
@@ -688,6 +731,17 @@ int fill_config_for(int64_t M, int64_t N) {
       best = c;
       best_t = t;
     }
+  }
+  // The mixed launch, when the 256 x 256 tiles leave a last wave at most half
+  // full after one or two whole waves: whole waves of tiles, then one wave of
+  // halves.  After three or more whole waves it measured within a few percent
+  // of the plain launch either way (a partly filled last wave runs at a
+  // higher clock under the power limit), so it is not used there.
+  const int64_t T = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t r = T % cus;
+  if (K % BK2 == 0 && T > cus && T < 3 * cus && r > 0 && 2 * r <= cus) {
+    const double t = (double)(T / cus) + kTileCost[1];
+    if (t < best_t - 1e-9) best = kMixed;
   }
   return best;
 }
@@ -743,7 +797,7 @@ extern "C" int bi_gemm_num_configs(void) { return kNumConfigs; }
 
 extern "C" int bi_gemm_fill_config_id(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 8 || (N & 7) || K < BK || K % BK) return -1;
-  return fill_config_for(M, N);
+  return fill_config_for(M, N, K);
 }
 
 extern "C" int bi_gemm_fill(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M,
@@ -751,7 +805,16 @@ extern "C" int bi_gemm_fill(const uint16_t *x, const uint16_t *w, uint16_t *y, i
                             void *stream) {
   const int st = validate(x, w, y, M, N, K, ldx, ldw, ldy);
   if (st != BI_OK || M == 0) return st;
-  return launch(fill_config_for(M, N), x, w, y, M, N, K, ldx, ldw, ldy, stream);
+  const int cfg = fill_config_for(M, N, K);
+  if (cfg != kMixed) return launch(cfg, x, w, y, M, N, K, ldx, ldw, ldy, stream);
+  const int64_t tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256, T = tiles_m * tiles_n;
+  const int64_t nfull = T - T % cu_count();
+  const int64_t grid = nfull + 2 * (T - nfull);
+  if (grid > 0x7FFFFFFF) return BI_ERR_SHAPE;
+  hipLaunchKernelGGL(gemm_mixed_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+                     (hipStream_t)stream, x, w, y, (int)M, (int)N, (int)K, ldx, ldw, ldy,
+                     (int)tiles_m, (int)tiles_n, (int)nfull);
+  return launch_status();
 }
 
 extern "C" int bi_gemm_with_config(int config, const uint16_t *x, const uint16_t *w, uint16_t *y,
