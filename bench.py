@@ -15,7 +15,9 @@ algorithmic TFLOP/s (2*M*N*K per GEMM, 2*M*R*K per shrink) over the timed
 steps.  ``roofline`` is for the dominant kernel (the 256x256-tile GEMM, which
 runs Q, U and D), timed with HIP events around its launches on the launch
 stream.  ``cpu_baseline`` is the fp64 CPU oracle timed on a bounded row sample
-of the same step.
+of the same step.  ``clock`` is the shader clock and socket power read during
+the untimed settle steps, and the dominant kernel's fraction of the MFMA peak
+scaled to that clock (the published peak assumes 2.4 GHz).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--M 4096]
        [--sweep FILE]   also time each kernel over an M sweep (JSONL to FILE)
@@ -35,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "batch-invariant bf16 GEMM TFLOP/s (% MFMA peak) over M; RMSNorm GB/s (% HBM)"
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
+SPEC_SCLK_MHZ = 2400.0        # the clock the published peaks assume
 K_MODEL, N_Q, N_KV, N_UP = 4096, 4096, 1024, 14336
 R_LORA = 16
 
@@ -52,9 +55,11 @@ def parse():
                              "splitk"])
     ap.add_argument("--iters", type=int, default=50, help="launches for --only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--settle", type=float, default=0.5,
+    ap.add_argument("--settle", type=float, default=2.5,
                     help="seconds of untimed steps before the warm-up steps, so the GPU "
-                         "clocks leave their idle state (a few 1 ms steps do not)")
+                         "clocks leave their idle state (a few 1 ms steps do not); the "
+                         "clock is read during them (the SMI table refreshes about once "
+                         "a second)")
     return ap.parse_args()
 
 
@@ -149,13 +154,16 @@ def main():
 
     # Untimed: let the clocks ramp from idle (measured: with only a handful of
     # warm-up steps the GEMMs run ~8 % slower than in steady state).
+    # The shader clock and socket power are sampled during these steps (a
+    # read-only query from a side thread), not during the timed ones.
     t_settle = time.time()
     settle_steps = 0
-    while time.time() - t_settle < args.settle:
-        for _ in range(20):
-            step(False)
-        settle_steps += 20
-        torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        while time.time() - t_settle < args.settle:
+            for _ in range(20):
+                step(False)
+            settle_steps += 20
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -197,6 +205,7 @@ def main():
         "roofline": roofline,
         "invariance": {"probe_rows": len(probes), "diff_bits_last_step": bits_after},
         "settle": {"seconds": args.settle, "untimed_steps": settle_steps},
+        "clock": clk.summary(achieved),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, g, ws_h, a, eps)
@@ -204,6 +213,91 @@ def main():
         out["sweep_file"] = args.sweep
         sweep(args.sweep, bi, torch, dev, to_dev)
     print(json.dumps(out), flush=True)
+
+
+class ClockSampler:
+    """Samples the card's shader clock (mean over its XCDs) and socket power
+    every ``period`` seconds from a background thread through the ROCm SMI
+    library's metrics table; read-only.  The firmware refreshes that table
+    about once a second (measured), so readings from the first ``skip``
+    seconds may still describe the time before the sampled work and are
+    dropped, and a reading repeated unchanged counts once.  Records nothing,
+    and says why, when the library cannot read exactly one card."""
+
+    def __init__(self, period: float = 0.05, skip: float = 1.0):
+        self.period = period
+        self.skip = skip
+        self.samples = []
+        self.err = None
+        self._thread = None
+        self._smi = None
+        import threading
+        self._stop = threading.Event()
+
+    def __enter__(self):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if len(handles) != 1:
+                raise RuntimeError(f"{len(handles)} GPUs visible to amdsmi")
+            self._handle = handles[0]
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        except Exception as e:  # no SMI access: the bench runs without clocks
+            self.err = repr(e)[:200]
+        return self
+
+    @staticmethod
+    def _num(v):
+        return float(v) if isinstance(v, (int, float)) and not isinstance(v, bool) and v > 0 else None
+
+    def _run(self):
+        t0 = time.time()
+        while not self._stop.is_set():
+            try:
+                m = self._smi.amdsmi_get_gpu_metrics_info(self._handle)
+            except Exception as e:
+                self.err = repr(e)[:200]
+                return
+            clks = [c for c in map(self._num, m.get("current_gfxclks") or []) if c]
+            if not clks and self._num(m.get("current_gfxclk")):
+                clks = [self._num(m.get("current_gfxclk"))]
+            power = self._num(m.get("current_socket_power")) or self._num(m.get("average_socket_power"))
+            if clks and time.time() - t0 >= self.skip:
+                r = (sum(clks) / len(clks), power)
+                if not self.samples or self.samples[-1] != r:
+                    self.samples.append(r)
+            self._stop.wait(self.period)
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        if self._smi is not None:
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:
+                pass
+        return False
+
+    def summary(self, achieved_tflops: float):
+        if not self.samples:
+            return {"source": "amdsmi gpu_metrics", "readings": 0,
+                    "error": self.err or f"no reading after the first {self.skip} s"}
+        mhz = [c for c, _ in self.samples]
+        watts = [w for _, w in self.samples if w]
+        mean = sum(mhz) / len(mhz)
+        peak_at_clock = PEAK_BF16_TFLOPS * mean / SPEC_SCLK_MHZ
+        return {"source": "amdsmi gpu_metrics, sampled during the untimed settle steps",
+                "readings": len(mhz), "sclk_mhz_mean": round(mean, 1),
+                "sclk_mhz_min": round(min(mhz), 1), "sclk_mhz_max": round(max(mhz), 1),
+                "spec_sclk_mhz": SPEC_SCLK_MHZ,
+                "socket_power_w_mean": round(sum(watts) / len(watts), 1) if watts else None,
+                "mfma_peak_at_mean_clock": round(peak_at_clock, 1),
+                "roofline_frac_at_mean_clock": round(achieved_tflops / peak_at_clock, 4)}
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_wide_kernel_256x256_llama8b_m4096_hbm.txt")
