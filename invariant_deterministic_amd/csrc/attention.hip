@@ -13,10 +13,10 @@
 // chunks follows the sequence's own length T_b only.
 //
 // Decode attention streams the whole cache, so it is bound by HBM bandwidth:
-// 2 * T_b * Hkv * D * 2 bytes of K and V per sequence.  Reads are coalesced:
-// keys in 64-byte pieces of 16 tokens per instruction (the matrix-core
-// layout), values as whole rows straight into LDS, loaded while the scores
-// are computed.
+// 2 * T_b * Hkv * D * 2 bytes of K and V per sequence.  Both are read as
+// whole 128-byte lines with the non-temporal hint: keys into registers, then
+// lane-permuted into the matrix-core layout; values as whole rows straight
+// into LDS, loaded while the scores are computed.
 //
 // Order of every output o[b][h][:] (G = H / Hkv query heads share key/value
 // head h / G; workgroup = 4 wavefronts):
@@ -86,7 +86,8 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
       const int row0 = (i * 4 + wv) * RPI;
       const int t = min(pass * VS + row0 + lane / LPR, n - 1);
       const int off = (int)(((int64_t)t * row_stride + (lane % LPR) * 8) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(vs + row0 * D), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(vs + row0 * D), 16, off, 0, 0,
+                                               kCpolNT);  // read once
     }
   };
 
@@ -94,8 +95,7 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
   // blocks of 32 (ascending), query heads as the A rows (zero past G), 16
   // tokens as the B columns.  Lane l supplies head / token (l & 15) and
   // d = 32j + 8(l >> 4) .. +7 of block j; it receives s for token (l & 15),
-  // heads 4(l >> 4) .. +3.  A token's 64-byte piece of block j is read by 4
-  // lanes, so one load instruction covers 16 tokens.
+  // heads 4(l >> 4) .. +3.
   bf16x8 qa[NJ];
   {
     const int g = lane & 15;
@@ -106,27 +106,30 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
       if (g >= G) qa[j] = bf16x8{};
     }
   }
-  const uint16_t *kb2 = kseq + (lane >> 4) * 8;
+  static_assert(NJ % 2 == 0, "keys are fetched as 128-byte lines, two d blocks each");
   const int tok = lane & 15;
+  const int q8 = lane >> 3, u8 = lane & 7;
 #pragma unroll 1
   for (int gb = 0; gb < NGRP; gb += GB) {
+    // Keys as whole 128-byte lines, permuted into the matrix-core layout.
     // Tokens at or past n load token n - 1 (in bounds, finite; masked below).
-    bf16x8 kf[GB][NJ];
+    LineOperand16<NJ / 2, true> kl[GB];
 #pragma unroll
     for (int i = 0; i < GB; ++i) {
-      const int t = min(wv * tpw + (gb + i) * 16 + tok, n - 1);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        kf[i][j] = __builtin_nontemporal_load(
-            reinterpret_cast<const bf16x8 *>(kb2 + (int64_t)t * row_stride + 32 * j));
+      const int t16 = wv * tpw + (gb + i) * 16;
+      const int tlo = min(t16 + q8, n - 1), thi = min(t16 + 8 + q8, n - 1);
+      kl[i].issue(kseq + (int64_t)tlo * row_stride + u8 * 8,
+                  kseq + (int64_t)thi * row_stride + (u8 ^ 4) * 8);
     }
     // The first pass of values loads while the scores are computed.
     if (gb == 0) issue_v(0);
 #pragma unroll
     for (int i = 0; i < GB; ++i) {
+      bf16x8 kf[NJ];
+      kl[i].place(kf, lane);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], kf[i][j], acc, 0, 0, 0);
+      for (int j = 0; j < NJ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], kf[j], acc, 0, 0, 0);
       const int t = wv * tpw + (gb + i) * 16 + tok;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {

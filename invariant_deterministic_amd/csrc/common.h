@@ -63,6 +63,57 @@ __device__ __forceinline__ void barrier_no_fence() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Cache-policy operand of the buffer loads: bit 1 is the non-temporal hint.
+constexpr int kCpolNT = 2;
+
+// A 16-row operand of v_mfma_f32_16x16x32_bf16 over 2*NP steps of 32 bf16:
+// lane l must hold row l & 15, k = 32t + 8(l >> 4) .. +7 of step t.  Loading
+// that layout directly makes each of 16 consecutive lanes touch a different
+// row, so every lane becomes a request of its own.  Here the loads fetch
+// whole 128-byte lines -- a line of one row is 64 k, two steps, and eight
+// consecutive lanes take it: lane 8q + u loads unit u (16 bytes) of row q
+// into lo and unit u ^ 4 of row 8 + q into hi -- and one select and one lane
+// permute per register then move every unit to the lane the matrix core
+// wants it in (the values, hence the products, are unchanged).
+//   issue(plo, phi): plo = &row q [8u], phi = &row (8 + q) [8(u ^ 4)], with
+//     q = lane >> 3, u = lane & 7; step pair g is read at +64g elements.
+//   place(out): out[t] for t < 2*NP in the matrix-core layout.
+template <int NP, bool NT>
+struct LineOperand16 {
+  u32x4 lo[NP], hi[NP];
+  __device__ __forceinline__ void issue(const uint16_t *plo, const uint16_t *phi) {
+#pragma unroll
+    for (int g = 0; g < NP; ++g) {
+      const u32x4 *a = reinterpret_cast<const u32x4 *>(plo + 64 * g);
+      const u32x4 *b = reinterpret_cast<const u32x4 *>(phi + 64 * g);
+      lo[g] = NT ? __builtin_nontemporal_load(a) : *a;
+      hi[g] = NT ? __builtin_nontemporal_load(b) : *b;
+    }
+  }
+  // Step 2g, lane r + 16c (r < 8) wants unit c of row r: lo of lane 8r + c;
+  // (r >= 8) unit c of row r: hi of lane 8(r-8) + 4 + c.  Step 2g+1 wants unit
+  // 4 + c: lo of lane 8r + 4 + c, or hi of lane 8(r-8) + c.  So lanes whose
+  // unit slot is below 4 offer lo for step 2g and hi for step 2g+1, the others
+  // the reverse, and one permute per register gathers each step.
+  __device__ __forceinline__ void place(bf16x8 *out, int lane) const {
+    const bool first = (lane & 4) == 0;
+    const int r = lane & 15, c = lane >> 4;
+    const int src0 = (r < 8 ? 8 * r + c : 8 * (r - 8) + 4 + c) * 4;
+    const int src1 = (r < 8 ? 8 * r + 4 + c : 8 * (r - 8) + c) * 4;
+#pragma unroll
+    for (int g = 0; g < NP; ++g) {
+      u32x4 t0, t1;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        t0[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src0, (int)(first ? lo[g][d] : hi[g][d]));
+        t1[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, (int)(first ? hi[g][d] : lo[g][d]));
+      }
+      out[2 * g] = __builtin_bit_cast(bf16x8, t0);
+      out[2 * g + 1] = __builtin_bit_cast(bf16x8, t1);
+    }
+  }
+};
+
 // Compute units of the current device (256 on MI355X if the query fails).
 inline int cu_count() {
   int dev = 0, n = 0;

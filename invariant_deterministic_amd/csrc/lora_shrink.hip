@@ -54,9 +54,6 @@ constexpr int kStep = 32;     // k per matrix-core step
 
 enum Mode { kStoreOut = 0, kStoreWs = 1, kAtomic = 2 };
 
-// Cache-policy operand of the buffer loads: bit 1 is the non-temporal hint.
-constexpr int kCpolNT = 2;
-
 // Operand roles of every kernel here: the A operand is the LoRA matrix
 // (16 ranks x 32 k), the B operand is x (32 k x 16 rows).  Lane l supplies
 // rank / row (l & 15) and k = step*32 + (l >> 4)*8 .. +7 of both operands, so
@@ -148,53 +145,6 @@ __global__ __launch_bounds__(kThreads) void shrink_partial_kernel(
   if (MODE == kStoreOut) *reinterpret_cast<f32x4 *>(out + (int64_t)m * ldo + r0) = acc;
   else *reinterpret_cast<f32x4 *>(out + ((int64_t)s * M + m) * kR + r0) = acc;
 }
-
-// A wavefront's chunk of a (16 ranks x STEPS*32 k, from column k0) for the
-// matrix core: lane l must end up with rank l & 15, k = t*32 + (l >> 4)*8 .. +7
-// of step t.  Loading that layout directly makes every lane touch a line of
-// its own (16 ranks per 16 lanes), 64 requests an instruction.  Here the loads
-// fetch whole 128-byte lines instead -- a line of one rank is 64 k, two steps,
-// and eight consecutive lanes take it: lane 8q + u loads unit u (16 bytes) of
-// rank q into lo and unit u ^ 4 of rank 8 + q into hi -- and one select and
-// one lane permute per register then move every unit to the lane the matrix
-// core wants it in.  The values are the same, so are the products.
-template <int STEPS>
-struct ALines {
-  static_assert(STEPS % 2 == 0, "a line holds two steps");
-  u32x4 lo[STEPS / 2], hi[STEPS / 2];
-  __device__ __forceinline__ void issue(const uint16_t *a, int64_t lda, int k0, int lane) {
-    const int q = lane >> 3, u = lane & 7;
-    const uint16_t *p0 = a + (int64_t)q * lda + k0 + u * 8;
-    const uint16_t *p1 = a + (int64_t)(8 + q) * lda + k0 + (u ^ 4) * 8;
-#pragma unroll
-    for (int g = 0; g < STEPS / 2; ++g) {
-      lo[g] = *reinterpret_cast<const u32x4 *>(p0 + g * 64);
-      hi[g] = *reinterpret_cast<const u32x4 *>(p1 + g * 64);
-    }
-  }
-  // Step 2g, lane r + 16c (r < 8) wants unit c of rank r: lo of lane 8r + c;
-  // (r >= 8) unit c of rank r: hi of lane 8(r-8) + 4 + c.  Step 2g+1 wants
-  // unit 4 + c: lo of lane 8r + 4 + c, or hi of lane 8(r-8) + c.  So lanes
-  // whose unit slot is below 4 offer lo for step 2g and hi for step 2g+1, the
-  // others the reverse, and one permute per register gathers each step.
-  __device__ __forceinline__ void place(bf16x8 *af, int lane) const {
-    const bool first = (lane & 4) == 0;
-    const int r = lane & 15, c = lane >> 4;
-    const int src0 = (r < 8 ? 8 * r + c : 8 * (r - 8) + 4 + c) * 4;
-    const int src1 = (r < 8 ? 8 * r + 4 + c : 8 * (r - 8) + c) * 4;
-#pragma unroll
-    for (int g = 0; g < STEPS / 2; ++g) {
-      u32x4 t0, t1;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        t0[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src0, (int)(first ? lo[g][d] : hi[g][d]));
-        t1[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, (int)(first ? hi[g][d] : lo[g][d]));
-      }
-      af[2 * g] = __builtin_bit_cast(bf16x8, t0);
-      af[2 * g + 1] = __builtin_bit_cast(bf16x8, t1);
-    }
-  }
-};
 
 // Stores (or adds) the partial of wavefront s for rows m0 .. m0+15 and, in the
 // folding modes, the fold of the S partials through LDS (part holds S x 64
@@ -310,8 +260,11 @@ __global__ __launch_bounds__(64 * S, 1) void shrink_staged_kernel(
   // The chunk of a first (whole-line loads, mostly cache hits, kept in
   // registers for the whole launch), then the first two pieces of x; a is
   // moved into the matrix-core layout while x is on its way.
-  ALines<STEPS> al;
-  al.issue(a, lda, k0, lane);
+  LineOperand16<STEPS / 2, false> al;
+  {
+    const int q = lane >> 3, u = lane & 7;
+    al.issue(a + (int64_t)q * lda + k0 + u * 8, a + (int64_t)(8 + q) * lda + k0 + (u ^ 4) * 8);
+  }
   __builtin_amdgcn_sched_barrier(0);
   issue(0);
   if (npieces > 1) issue(1);
