@@ -77,7 +77,8 @@ constexpr int kCpolNT = 2;
 // wants it in (the values, hence the products, are unchanged).
 //   issue(plo, phi): plo = &row q [8u], phi = &row (8 + q) [8(u ^ 4)], with
 //     q = lane >> 3, u = lane & 7; step pair g is read at +64g elements.
-//   place(out): out[t] for t < 2*NP in the matrix-core layout.
+//   place(out): out[t] for t < 2*NP in the matrix-core layout; place_pair(g,
+//     out): steps 2g, 2g + 1 only.
 template <int NP, bool NT>
 struct LineOperand16 {
   u32x4 lo[NP], hi[NP];
@@ -95,22 +96,24 @@ struct LineOperand16 {
   // 4 + c: lo of lane 8r + 4 + c, or hi of lane 8(r-8) + c.  So lanes whose
   // unit slot is below 4 offer lo for step 2g and hi for step 2g+1, the others
   // the reverse, and one permute per register gathers each step.
-  __device__ __forceinline__ void place(bf16x8 *out, int lane) const {
+  // Steps 2g and 2g + 1 -> out[0], out[1].
+  __device__ __forceinline__ void place_pair(int g, bf16x8 *out, int lane) const {
     const bool first = (lane & 4) == 0;
     const int r = lane & 15, c = lane >> 4;
     const int src0 = (r < 8 ? 8 * r + c : 8 * (r - 8) + 4 + c) * 4;
     const int src1 = (r < 8 ? 8 * r + 4 + c : 8 * (r - 8) + c) * 4;
+    u32x4 t0, t1;
 #pragma unroll
-    for (int g = 0; g < NP; ++g) {
-      u32x4 t0, t1;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        t0[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src0, (int)(first ? lo[g][d] : hi[g][d]));
-        t1[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, (int)(first ? hi[g][d] : lo[g][d]));
-      }
-      out[2 * g] = __builtin_bit_cast(bf16x8, t0);
-      out[2 * g + 1] = __builtin_bit_cast(bf16x8, t1);
+    for (int d = 0; d < 4; ++d) {
+      t0[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src0, (int)(first ? lo[g][d] : hi[g][d]));
+      t1[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, (int)(first ? hi[g][d] : lo[g][d]));
     }
+    out[0] = __builtin_bit_cast(bf16x8, t0);
+    out[1] = __builtin_bit_cast(bf16x8, t1);
+  }
+  __device__ __forceinline__ void place(bf16x8 *out, int lane) const {
+#pragma unroll
+    for (int g = 0; g < NP; ++g) place_pair(g, out + 2 * g, lane);
   }
 };
 

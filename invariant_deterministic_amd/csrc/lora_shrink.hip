@@ -37,8 +37,9 @@
 //     blocks, so a is fetched once per workgroup rather than once per row
 //     block.
 //   streamed kernel (other splits, and the two-pass partials): x and a go
-//     straight to registers in the matrix-core layout, a group of 8 steps per
-//     load batch, up to 3 batches in flight.
+//     straight to registers as whole lines, a group of 8 steps per load
+//     batch, up to 3 batches in flight, and are lane-permuted into the
+//     matrix-core layout before their steps.
 // Every kernel feeds the matrix core the same operands in the same step
 // order, so they all produce the same bits.
 #include "common.h"
@@ -63,25 +64,49 @@ __device__ __forceinline__ f32x4 mfma_step(bf16x8 a, bf16x8 x, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, x, acc, 0, 0, 0);
 }
 
-// Partial of one wavefront over STEPS steps (compile-time count): loads go out
-// in batches of G steps, DEPTH batches ahead of the math (64 registers a batch,
-// so DEPTH is capped by the wavefronts a workgroup puts on each SIMD).  xp / ap point at
-// this lane's first 16-byte piece of x and a.
+// Where one lane reads its operands: the matrix-core layout (mx / ma: row
+// l & 15, 16-byte unit l >> 4 of each step) for the one-step-at-a-time path,
+// and the whole-line layout of LineOperand16 (lo / hi rows of x and a) for
+// the streamed path.  Rows of x past M read a copy of the last row, never
+// stored.  All point at column k0 of the chunk.
+struct ChunkPtrs {
+  const bf16x8 *mx, *ma;
+  const uint16_t *xlo, *xhi, *alo, *ahi;
+};
+__device__ __forceinline__ ChunkPtrs chunk_ptrs(const uint16_t *x, const uint16_t *a, int M,
+                                                int64_t ldx, int64_t lda, int m0, int k0,
+                                                int lane) {
+  const auto row = [&](int r) { return (int64_t)(r < M ? r : M - 1); };
+  const int q = lane >> 3, u = lane & 7;
+  const int koff = (lane >> 4) * 8;
+  ChunkPtrs p;
+  p.mx = reinterpret_cast<const bf16x8 *>(x + row(m0 + (lane & 15)) * ldx + k0 + koff);
+  p.ma = reinterpret_cast<const bf16x8 *>(a + (int64_t)(lane & 15) * lda + k0 + koff);
+  p.xlo = x + row(m0 + q) * ldx + k0 + u * 8;
+  p.xhi = x + row(m0 + 8 + q) * ldx + k0 + (u ^ 4) * 8;
+  p.alo = a + (int64_t)q * lda + k0 + u * 8;
+  p.ahi = a + (int64_t)(8 + q) * lda + k0 + (u ^ 4) * 8;
+  return p;
+}
+
+// Partial of one wavefront over STEPS steps (compile-time count): x and a are
+// fetched as whole lines in batches of G steps, DEPTH batches ahead of the
+// math (64 registers a batch, so DEPTH is capped by the wavefronts a
+// workgroup puts on each SIMD), and lane-permuted into the matrix-core layout
+// just before their steps.
 template <int STEPS, int MAXDEPTH>
-__device__ __forceinline__ f32x4 chunk_streamed(const bf16x8 *xp, const bf16x8 *ap) {
+__device__ __forceinline__ f32x4 chunk_streamed(const ChunkPtrs &p, int lane) {
   constexpr int G = STEPS < 8 ? STEPS : 8;
   constexpr int NG = STEPS / G;
   constexpr int DEPTH = NG < MAXDEPTH ? NG : MAXDEPTH;
-  static_assert(STEPS % G == 0, "step count");
-  bf16x8 xf[DEPTH][G], af[DEPTH][G];
+  static_assert(STEPS % G == 0 && G % 2 == 0, "step count");
+  LineOperand16<G / 2, true> xl[DEPTH];
+  LineOperand16<G / 2, false> al[DEPTH];
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int g = 0; g < DEPTH; ++g) {
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      xf[g][i] = __builtin_nontemporal_load(xp + (g * G + i) * (kStep / 8));
-      af[g][i] = ap[(g * G + i) * (kStep / 8)];
-    }
+    xl[g].issue(p.xlo + g * G * kStep, p.xhi + g * G * kStep);
+    al[g].issue(p.alo + g * G * kStep, p.ahi + g * G * kStep);
   }
   // Keep the batch together: without this the scheduler trades loads in flight
   // for registers.
@@ -89,13 +114,16 @@ __device__ __forceinline__ f32x4 chunk_streamed(const bf16x8 *xp, const bf16x8 *
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
 #pragma unroll
-    for (int i = 0; i < G; ++i) acc = mfma_step(af[g % DEPTH][i], xf[g % DEPTH][i], acc);
+    for (int pr = 0; pr < G / 2; ++pr) {
+      bf16x8 xf[2], af[2];
+      xl[g % DEPTH].place_pair(pr, xf, lane);
+      al[g % DEPTH].place_pair(pr, af, lane);
+      acc = mfma_step(af[0], xf[0], acc);
+      acc = mfma_step(af[1], xf[1], acc);
+    }
     if (g + DEPTH < NG) {
-#pragma unroll
-      for (int i = 0; i < G; ++i) {
-        xf[g % DEPTH][i] = __builtin_nontemporal_load(xp + ((g + DEPTH) * G + i) * (kStep / 8));
-        af[g % DEPTH][i] = ap[((g + DEPTH) * G + i) * (kStep / 8)];
-      }
+      xl[g % DEPTH].issue(p.xlo + (g + DEPTH) * G * kStep, p.xhi + (g + DEPTH) * G * kStep);
+      al[g % DEPTH].issue(p.alo + (g + DEPTH) * G * kStep, p.ahi + (g + DEPTH) * G * kStep);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -103,7 +131,7 @@ __device__ __forceinline__ f32x4 chunk_streamed(const bf16x8 *xp, const bf16x8 *
 }
 
 // Same partial for a step count known only at run time (shapes outside the
-// compiled set): one step at a time.
+// compiled set): one step at a time, straight from the matrix-core layout.
 __device__ __forceinline__ f32x4 chunk_plain(const bf16x8 *xp, const bf16x8 *ap, int steps) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < steps; ++t)
@@ -112,12 +140,12 @@ __device__ __forceinline__ f32x4 chunk_plain(const bf16x8 *xp, const bf16x8 *ap,
 }
 
 template <int STEPS, int MAXDEPTH>
-__device__ __forceinline__ f32x4 chunk_partial(const bf16x8 *xp, const bf16x8 *ap, int steps) {
+__device__ __forceinline__ f32x4 chunk_partial(const ChunkPtrs &p, int steps, int lane) {
   if constexpr (STEPS > 0) {
     (void)steps;
-    return chunk_streamed<STEPS, MAXDEPTH>(xp, ap);
+    return chunk_streamed<STEPS, MAXDEPTH>(p, lane);
   } else {
-    return chunk_plain(xp, ap, steps);
+    return chunk_plain(p.mx, p.ma, steps);
   }
 }
 
@@ -132,13 +160,8 @@ __global__ __launch_bounds__(kThreads) void shrink_partial_kernel(
   const int mw = blockIdx.x * kRowsPerBlock + wv * kRowsPerWave;
   if (mw >= M) return;  // every row of this wavefront is past the batch
   const int s = blockIdx.y;
-  const int k0 = s * chunk;
-  int gm = mw + (lane & 15);
-  gm = gm < M ? gm : M - 1;  // rows past M read a copy of the last row, never stored
-  const int koff = (lane >> 4) * 8;
-  const bf16x8 *xp = reinterpret_cast<const bf16x8 *>(x + (int64_t)gm * ldx + k0 + koff);
-  const bf16x8 *ap = reinterpret_cast<const bf16x8 *>(a + (int64_t)(lane & 15) * lda + k0 + koff);
-  const f32x4 acc = chunk_partial<STEPS, 3>(xp, ap, chunk / kStep);
+  const f32x4 acc =
+      chunk_partial<STEPS, 3>(chunk_ptrs(x, a, M, ldx, lda, mw, s * chunk, lane), chunk / kStep, lane);
   const int m = mw + (lane & 15);
   if (m >= M) return;
   const int r0 = (lane >> 4) * 4;
@@ -188,13 +211,8 @@ __global__ __launch_bounds__(64 * S) void shrink_fused_kernel(
   const int s = threadIdx.x >> 6;
   const int m0 = blockIdx.x * kRowsPerWave;
   const int chunk = K / S;
-  const int k0 = s * chunk;
-  int gm = m0 + (lane & 15);
-  gm = gm < M ? gm : M - 1;  // rows past M read a copy of the last row, never stored
-  const int koff = (lane >> 4) * 8;
-  const bf16x8 *xp = reinterpret_cast<const bf16x8 *>(x + (int64_t)gm * ldx + k0 + koff);
-  const bf16x8 *ap = reinterpret_cast<const bf16x8 *>(a + (int64_t)(lane & 15) * lda + k0 + koff);
-  const f32x4 acc = chunk_partial<STEPS, (S >= 16 ? 1 : 3)>(xp, ap, chunk / kStep);
+  const f32x4 acc = chunk_partial<STEPS, (S >= 16 ? 1 : 3)>(
+      chunk_ptrs(x, a, M, ldx, lda, m0, s * chunk, lane), chunk / kStep, lane);
   __shared__ f32x4 part[S][64];
   emit<S, MODE>(acc, part, y, ws, M, ldy, m0, s, lane);
 }
@@ -346,13 +364,8 @@ __global__ __launch_bounds__(64 * kExpWaves, 1) void shrink_expand_kernel(
   __shared__ float ls[kRowsPerWave][kR];
   if (s < S) {
     const int chunk = K / S;
-    const int k0 = s * chunk;
-    int gm = m0 + (lane & 15);
-    gm = gm < M ? gm : M - 1;  // rows past M read a copy of the last row, never stored
-    const int koff = (lane >> 4) * 8;
-    const bf16x8 *xp = reinterpret_cast<const bf16x8 *>(x + (int64_t)gm * ldx + k0 + koff);
-    const bf16x8 *ap = reinterpret_cast<const bf16x8 *>(a + (int64_t)(lane & 15) * lda + k0 + koff);
-    part[s][lane] = chunk_partial<STEPS, 1>(xp, ap, chunk / kStep);
+    part[s][lane] = chunk_partial<STEPS, 1>(chunk_ptrs(x, a, M, ldx, lda, m0, s * chunk, lane),
+                                            chunk / kStep, lane);
   }
   __syncthreads();
   if (s == 0) {
