@@ -13,8 +13,9 @@
 // per SIMD cycle is close to the HBM time).  Each wavefront owns 512
 // consecutive columns -- 8 per lane, 16 bytes of base and of y -- for a run of
 // rows: its lanes hold their 8 columns of b, widened to fp32, in registers for
-// the whole run, each row's 16 values of l arrive through the scalar cache,
-// and the row loop keeps two batches of kAhead rows of base loads in flight.
+// the whole run (staged through LDS once per workgroup, whole-line loads),
+// each row's 16 values of l arrive through the scalar cache, and the row loop
+// keeps two batches of kAhead rows of base loads in flight.
 #include "common.h"
 
 namespace bi {
@@ -34,9 +35,28 @@ __global__ __launch_bounds__(kThreads) void lora_expand_kernel(
     float scale, int rpw) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * kCols + lane * 8;
+  const int slice0 = blockIdx.x * kCols;
+  const int n0 = slice0 + lane * 8;
   const bool col_ok = n0 < N;  // N is a multiple of 8: a lane's 8 columns are all in or all out
   const int nn = col_ok ? n0 : N - 8;
+
+  // The slice's 512 rows of b (16 KiB, the same for the 4 wavefronts) go to
+  // LDS once through whole-line loads: thread t moves 16-byte units t, t +
+  // 256, ... of the slice's rows.  The 16 units a lane needs (its 8 rows)
+  // form block L = lane; unit c of block L is stored at c ^ (L & 15), so the
+  // lanes of one read touch different banks.  Rows past N load row N - 1
+  // (unused).
+  __shared__ u32x4 bs[kCols * kR / 8];
+#pragma unroll
+  for (int i = 0; i < kCols * kR / 8 / kThreads; ++i) {
+    const int u = threadIdx.x + i * kThreads;
+    const int L = u >> 4, c = u & 15;
+    const int n = min(slice0 + (u >> 1), N - 1);
+    bs[L * 16 + (c ^ (L & 15))] =
+        *reinterpret_cast<const u32x4 *>(b + (int64_t)n * ldb + (u & 1) * 8);
+  }
+  __syncthreads();
+
   const int m_begin = (blockIdx.y * 4 + wv) * rpw;
   if (m_begin >= M) return;
   const int m_end = min(M, m_begin + rpw);
@@ -45,10 +65,11 @@ __global__ __launch_bounds__(kThreads) void lora_expand_kernel(
   // registers for the whole run of rows: the row loop is then 16 fused
   // multiply-adds an output and nothing else per rank.
   float bf[8][kR];
+  const int L = (nn - slice0) >> 3;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const u32x4 *br = reinterpret_cast<const u32x4 *>(b + (int64_t)(nn + j) * ldb);
-    const u32x4 w0 = br[0], w1 = br[1];
+    const u32x4 w0 = bs[L * 16 + ((2 * j) ^ (L & 15))];
+    const u32x4 w1 = bs[L * 16 + ((2 * j + 1) ^ (L & 15))];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       bf[j][2 * i] = lo_bf16(w0[i]);
