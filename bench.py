@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--only", default=None,
                     choices=["gemm", "gemm_kv", "gemm_up", "gemm_down", "rmsnorm", "shrink_det8",
                              "shrink_two_pass", "shrink_atomic8", "shrink_unsplit", "copy",
-                             "splitk"])
+                             "splitk", "attention", "expand"])
     ap.add_argument("--iters", type=int, default=50, help="launches for --only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle", type=float, default=2.5,
@@ -595,9 +595,30 @@ def run_only(args, bi, torch, dev, X, G, H, Wq, Wkv, Wup, Wdown, U, A, L, WS, La
             ws = torch.empty(bi.bi_gemm_splitk_workspace_bytes(ms, w.shape[0], S),
                              dtype=torch.uint8, device=dev)
             sk.append((inp[:ms], w, y[:ms], S, ws))
+    if args.only == "attention":
+        # decode attention at Llama-3-8B heads, 64 sequences of 4096 tokens
+        # (1 GiB of K and V), split 256
+        B, T, Hh, Hkv, Dh = 64, 4096, 32, 8, 128
+        q = torch.randn((B, Hh, Dh), device=dev).to(torch.bfloat16)
+        kc = torch.randn((B, T, Hkv, Dh), device=dev).to(torch.bfloat16)
+        vc = torch.randn((B, T, Hkv, Dh), device=dev).to(torch.bfloat16)
+        lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+        o = torch.empty((B, Hh, Dh), dtype=torch.bfloat16, device=dev)
+        aws = torch.empty(bi.bi_decode_attention_workspace_bytes(B, Hh, T, Dh, 256),
+                          dtype=torch.uint8, device=dev)
+    if args.only == "expand":
+        # LoRA expand at d_model 4096, rank 16, from the shrink output
+        bexp = torch.randn((Wq.shape[0], L.shape[1]), device=dev).to(torch.bfloat16)
+        yexp = torch.empty((H.shape[0], Wq.shape[0]), dtype=torch.bfloat16, device=dev)
+        base = torch.randn(yexp.shape, device=dev).to(torch.bfloat16)
+        bi.bi_lora_shrink(H, A, y=L, split_k=8)
     torch.cuda.synchronize()
     for _ in range(n):
-        if args.only == "splitk":
+        if args.only == "attention":
+            bi.bi_decode_attention(q, kc, vc, lens, o=o, split_size=256, ws=aws)
+        elif args.only == "expand":
+            bi.bi_lora_expand(L, bexp, base=base, y=yexp)
+        elif args.only == "splitk":
             for inp, w, y, S, ws in sk:
                 bi.bi_gemm_splitk(inp, w, y=y, split_k=S, ws=ws)
         elif args.only == "gemm":
