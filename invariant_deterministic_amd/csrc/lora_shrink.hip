@@ -172,10 +172,12 @@ __global__ __launch_bounds__(kThreads) void shrink_partial_kernel(
 // Stores (or adds) the partial of wavefront s for rows m0 .. m0+15 and, in the
 // folding modes, the fold of the S partials through LDS (part holds S x 64
 // lanes; the caller places a barrier between the writes and wavefront 0's read).
-template <int S, int MODE>
+template <int S, int MODE, int RB = kRowsPerWave>
 __device__ __forceinline__ void emit(f32x4 acc, f32x4 (*part)[64], float *y, float *ws, int M,
                                      int64_t ldy, int m0, int s, int lane) {
-  const int m = m0 + (lane & 15);
+  // RB < 16: the block has RB rows; lanes of the matrix-core rows past them
+  // hold copies and store nothing
+  const int m = (lane & 15) < RB ? m0 + (lane & 15) : M;
   const int r0 = (lane >> 4) * 4;
   if (MODE == kAtomic) {
     if (m < M) {
@@ -217,19 +219,22 @@ __global__ __launch_bounds__(64 * S) void shrink_fused_kernel(
   emit<S, MODE>(acc, part, y, ws, M, ldy, m0, s, lane);
 }
 
-// Staged fused kernel, S = 8 or 16 wavefronts, STEPS steps per chunk.
+// Staged fused kernel, S = 8 or 16 wavefronts, STEPS steps per chunk, row
+// blocks of RB = 16 or 8 rows.
 //
-// A piece is 16 rows x PS steps of one wavefront's chunk (PS * 64 bytes a
+// A piece is RB rows x PS steps of one wavefront's chunk (PS * 64 bytes a
 // row); each wavefront owns a ring of two pieces in LDS.  One direct-to-LDS
 // instruction moves 1 KiB = 16/PS whole row segments; lane l of instruction i
 // loads row i*(16/PS) + l/U (U = PS*4 sixteen-byte units a row), unit
 // (l % U) ^ row, so unit u of row r sits at position u ^ r: a matrix-core read
 // (16 rows, one unit each, per 16 lanes) then touches 16 different 16-byte
-// bank groups.  The LDS of a workgroup is S*16 KiB of pieces plus two S x 1 KiB
-// fold buffers (144 KiB for S = 8, 160 KiB for S = 16): one workgroup per CU.  The pieces of a wavefront run block after block over the
-// workgroup's row blocks (blockIdx.x, + gridDim.x, ...); while one is read, the
-// next is in flight.
-template <int S, int STEPS, int MODE>
+// bank groups.  With RB = 8 the matrix core's rows 8-15 read rows 0-7 again
+// and their results are dropped.  At RB = 16 the LDS of a workgroup is S*16
+// KiB of pieces plus two S x 1 KiB fold buffers (144 KiB for S = 8, 160 KiB
+// for S = 16): one workgroup per CU.  The pieces of a wavefront run block
+// after block over the workgroup's row blocks (blockIdx.x, + gridDim.x, ...);
+// while one is read, the next is in flight.
+template <int S, int STEPS, int MODE, int RB>
 __global__ __launch_bounds__(64 * S, 1) void shrink_staged_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ a, float *__restrict__ y,
     float *__restrict__ ws, int M, int K, int64_t ldx, int64_t lda, int64_t ldy, int nblocks) {
@@ -238,9 +243,10 @@ __global__ __launch_bounds__(64 * S, 1) void shrink_staged_kernel(
   constexpr int ROWB = PS * 64;              // bytes of one row in a piece
   constexpr int U = ROWB / 16;               // 16-byte units of one row in a piece
   constexpr int RPI = 1024 / ROWB;           // rows per load instruction
-  constexpr int NI = 16 / RPI;               // load instructions per piece (= PS)
-  constexpr int PIECE = 16 * ROWB;
+  constexpr int NI = RB / RPI;               // load instructions per piece
+  constexpr int PIECE = RB * ROWB;
   static_assert(S * PS == 64 && STEPS % PS == 0 && U >= 16 && NP % 2 == 0, "staged shape");
+  static_assert((RB == 16 || RB == 8) && NI >= 1, "rows per block");
   // The two slots are separate LDS objects: the compiler's wait counting can
   // then tell that a read of one slot does not depend on a load into the other.
   __shared__ __attribute__((aligned(1024))) char xs0[S][PIECE];
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(64 * S, 1) void shrink_staged_kernel(
 
   // Piece j of this wavefront -> LDS slot j & 1.
   auto issue = [&](int j) {
-    const int m0 = ((int)blockIdx.x + (j / NP) * (int)gridDim.x) * kRowsPerWave;
+    const int m0 = ((int)blockIdx.x + (j / NP) * (int)gridDim.x) * RB;
     const int kp = k0 + (j % NP) * PS * kStep;
     const uint16_t *base = x + (int64_t)m0 * ldx;
     const int64_t left = xbytes - (int64_t)m0 * ldx * 2;
@@ -289,8 +295,9 @@ __global__ __launch_bounds__(64 * S, 1) void shrink_staged_kernel(
   __builtin_amdgcn_sched_barrier(0);
   bf16x8 af[STEPS];
   al.place(af, lane);
-  // Matrix-core steps over piece j (slot j & 1) into acc.
-  const int r = lane & 15;
+  // Matrix-core steps over piece j (slot j & 1) into acc.  With 8-row blocks
+  // the matrix core's rows 8-15 repeat rows 0-7 and are never stored.
+  const int r = (lane & 15) % RB;
   auto compute = [&](int j, int p, f32x4 &acc) {
     const char *slot = (j & 1) ? xs1[s] : xs0[s];
     bf16x8 xv[PS];
@@ -320,8 +327,8 @@ __global__ __launch_bounds__(64 * S, 1) void shrink_staged_kernel(
       issue(j + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
-    const int m0 = ((int)blockIdx.x + bi * (int)gridDim.x) * kRowsPerWave;
-    emit<S, MODE>(acc, part[bi & 1], y, ws, M, ldy, m0, s, lane);
+    const int m0 = ((int)blockIdx.x + bi * (int)gridDim.x) * RB;
+    emit<S, MODE, RB>(acc, part[bi & 1], y, ws, M, ldy, m0, s, lane);
   }
   {  // last block: pieces npieces - NP .. npieces - 1; the first two are in
      // flight already, each later one is issued two pieces ahead (NP > 2)
@@ -335,8 +342,8 @@ __global__ __launch_bounds__(64 * S, 1) void shrink_staged_kernel(
       if (p + 2 < NP) issue(j + 2);
       __builtin_amdgcn_sched_barrier(0);
     }
-    const int m0 = ((int)blockIdx.x + bi * (int)gridDim.x) * kRowsPerWave;
-    emit<S, MODE>(acc, part[bi & 1], y, ws, M, ldy, m0, s, lane);
+    const int m0 = ((int)blockIdx.x + bi * (int)gridDim.x) * RB;
+    emit<S, MODE, RB>(acc, part[bi & 1], y, ws, M, ldy, m0, s, lane);
   }
 }
 
@@ -507,12 +514,27 @@ void launch_streamed(dim3 grid, hipStream_t st, const uint16_t *x, const uint16_
                      (int)M, (int)K, ldx, lda, ldy);
 }
 
+// Row blocks of 16 rows, one workgroup per CU, persistent over the blocks;
+// when 16-row blocks would leave at least half of the CUs idle (M <= 8 rows
+// per CU), blocks of 8 rows instead, twice as many workgroups.  Both run the
+// same matrix-core steps on every row, so the choice changes no bit
+// (measured at K = 4096: M = 64: 5.6 -> 4.7 us, M = 2048: 6.3 -> 5.9 us; at
+// M = 4096 the 8-row blocks, two workgroups per CU, were slower).
 template <int S, int STEPS, int MODE>
-void launch_staged(int grid, int nblocks, hipStream_t st, const uint16_t *x, const uint16_t *a,
-                   float *y, float *ws, int64_t M, int64_t K, int64_t ldx, int64_t lda,
-                   int64_t ldy) {
-  hipLaunchKernelGGL((shrink_staged_kernel<S, STEPS, MODE>), dim3(grid), dim3(64 * S), 0, st, x,
-                     a, y, ws, (int)M, (int)K, ldx, lda, ldy, nblocks);
+void launch_staged(hipStream_t st, const uint16_t *x, const uint16_t *a, float *y, float *ws,
+                   int64_t M, int64_t K, int64_t ldx, int64_t lda, int64_t ldy) {
+  const int64_t cus = cu_count();
+  if (M <= 8 * cus) {
+    const int64_t nblocks = (M + 7) / 8;
+    hipLaunchKernelGGL((shrink_staged_kernel<S, STEPS, MODE, 8>), dim3((unsigned)nblocks),
+                       dim3(64 * S), 0, st, x, a, y, ws, (int)M, (int)K, ldx, lda, ldy,
+                       (int)nblocks);
+  } else {
+    const int64_t nblocks = (M + kRowsPerWave - 1) / kRowsPerWave;
+    const int grid = (int)(nblocks < cus ? nblocks : cus);
+    hipLaunchKernelGGL((shrink_staged_kernel<S, STEPS, MODE, 16>), dim3(grid), dim3(64 * S), 0,
+                       st, x, a, y, ws, (int)M, (int)K, ldx, lda, ldy, (int)nblocks);
+  }
 }
 
 // One fused launch: the staged kernel for the deterministic splits (S = 8, 16)
@@ -525,10 +547,9 @@ void launch_fused(int S, hipStream_t st, const uint16_t *x, const uint16_t *a, f
   // the staged loads address x with 32-bit byte offsets inside a 16-row block
   if (((S == 8 && steps == 16) || (S == 16 && (steps == 8 || steps == 16))) &&
       ldx < (int64_t(1) << 26)) {
-    const int grid = (int)(nblocks < cu_count() ? nblocks : cu_count());
-    if (S == 8) launch_staged<8, 16, MODE>(grid, (int)nblocks, st, x, a, y, ws, M, K, ldx, lda, ldy);
-    else if (steps == 16) launch_staged<16, 16, MODE>(grid, (int)nblocks, st, x, a, y, ws, M, K, ldx, lda, ldy);
-    else launch_staged<16, 8, MODE>(grid, (int)nblocks, st, x, a, y, ws, M, K, ldx, lda, ldy);
+    if (S == 8) launch_staged<8, 16, MODE>(st, x, a, y, ws, M, K, ldx, lda, ldy);
+    else if (steps == 16) launch_staged<16, 16, MODE>(st, x, a, y, ws, M, K, ldx, lda, ldy);
+    else launch_staged<16, 8, MODE>(st, x, a, y, ws, M, K, ldx, lda, ldy);
     return;
   }
   const dim3 grid((unsigned)nblocks);
