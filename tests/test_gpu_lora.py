@@ -228,3 +228,31 @@ def test_shrink_staged_persistent_blocks(bi, K, split):
     X, A = dev_bf16(x), dev_bf16(a)
     say(f"shrink staged K={K} split={split} M={M}")
     assert np.array_equal(host_f32(bi.bi_lora_shrink(X, A, split_k=split)), want)
+
+
+@pytest.mark.parametrize("M", [100, 3000])
+def test_shrink_strided_inputs_same_bits(bi, M):
+    """x and a as column slices of wider buffers (row strides K + 64 and K + 8
+    elements): every path reads rows through the stride, so the bits equal
+    those of the contiguous inputs.  M = 100 runs the 8-row blocks of the
+    staged kernel, M = 3000 the 16-row ones; split 4 and the unsplit pass run
+    the streamed kernel."""
+    x, a = workloads.lora_inputs(M)
+    K = x.shape[1]
+    X, A = dev_bf16(x), dev_bf16(a)
+    Xw = torch.zeros((M, K + 64), dtype=X.dtype, device="cuda")
+    Aw = torch.zeros((a.shape[0], K + 8), dtype=A.dtype, device="cuda")
+    Xw[:, 32:32 + K] = X
+    Aw[:, :K] = A
+    Xs, As = Xw[:, 32:32 + K], Aw[:, :K]
+    assert Xs.stride(0) == K + 64 and As.stride(0) == K + 8
+    ref = oracle.lora_shrink(x, a)
+    for name, fn in (("det8", lambda xx, aa: bi.bi_lora_shrink(xx, aa, split_k=8)),
+                     ("split4", lambda xx, aa: bi.bi_lora_shrink(xx, aa, split_k=4)),
+                     ("unsplit", lambda xx, aa: bi.bi_lora_shrink(xx, aa, split_k=1)),
+                     ("two_pass", lambda xx, aa: bi.bi_lora_shrink_two_pass(xx, aa, split_k=8))):
+        say(f"shrink strided inputs {name} M={M}")
+        dense = host_u32(fn(X, A))
+        strided = host_u32(fn(Xs, As))
+        assert np.array_equal(dense, strided), name
+        check_f32(strided.view(np.float32), ref, f"strided {name} M={M}")

@@ -116,3 +116,30 @@ def test_shrink_expand_parity_invariance_and_in_place(bi):
     inplace = BASE.clone()
     bi.bi_lora_shrink_expand(X, A, B, base=inplace, y=inplace, scale=0.5)
     assert np.array_equal(host_u16(inplace), y)
+
+
+@pytest.mark.parametrize("N", [1032, 4096])
+def test_expand_strided_operands_same_bits(bi, N):
+    """l, b, base and y as slices of wider buffers (row strides 20, 24, N + 8
+    and N + 16 elements): the same bits as with contiguous operands.  N = 1032
+    leaves a last column slice of 8 columns, whose b rows past N are never
+    used."""
+    M = 77
+    l = synth.rng(910).standard_normal((M, 16)).astype(np.float32)
+    b = synth.normal_bf16((N, 16), 911, std=0.05)
+    base = synth.normal_bf16((M, N), 912)
+    L, B, BASE = torch.from_numpy(l).cuda(), dev_bf16(b), dev_bf16(base)
+    dense = host_u16(bi.bi_lora_expand(L, B, BASE, scale=0.75))
+    Lw = torch.zeros((M, 20), dtype=torch.float32, device="cuda")
+    Bw = torch.zeros((N, 24), dtype=B.dtype, device="cuda")
+    Basew = torch.zeros((M, N + 8), dtype=BASE.dtype, device="cuda")
+    Yw = torch.full((M, N + 16), 3.0, dtype=BASE.dtype, device="cuda")
+    Lw[:, :16] = L
+    Bw[:, 8:24] = B
+    Basew[:, :N] = BASE
+    say(f"expand strided N={N}")
+    bi.bi_lora_expand(Lw[:, :16], Bw[:, 8:24], Basew[:, :N], y=Yw[:, :N], scale=0.75)
+    yw = host_u16(Yw)
+    assert np.array_equal(yw[:, :N], dense)
+    assert np.all(yw[:, N:] == host_u16(torch.full((1,), 3.0, dtype=BASE.dtype))[0])
+    check_bf16(dense, oracle.lora_expand(l, b, base, scale=0.75), f"expand N={N}")
