@@ -16,7 +16,8 @@
 //
 // Three ways to run it, all computing the same partials p_s:
 //   fused     (bi_lora_shrink): one kernel.  A workgroup is S wavefronts over
-//             16-row blocks; wavefront s computes p_s, the S partials meet in
+//             row blocks (16 rows; 8 for small batches); wavefront s computes
+//             p_s, the S partials meet in
 //             LDS (the on-chip fp32 workspace) and wavefront 0 folds them in
 //             order.  No second launch, no atomics, no counters.
 //   two-pass  (bi_lora_shrink_two_pass): the split spans workgroups; partials go
