@@ -640,41 +640,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_partial_kernel(
 }
 
 // Fixed-order split-K combine: y[m][n] = bf16(((p_0 + p_1) + ...) + p_{S-1}),
-// eight outputs per thread.
+// four outputs per thread.  All loads of a group of up to kCombineGroup
+// partials are issued before its adds, which still run in s order, so the
+// fold costs one memory round trip per group (one in all the splits used
+// here); the skinny batches this path serves give the kernel few threads, so
+// its time is that latency.
+constexpr int kCombineGroup = 32;
 __global__ __launch_bounds__(kThreads) void gemm_splitk_combine_kernel(
     const float *__restrict__ ws, uint16_t *__restrict__ y, int M, int N, int S, int64_t ldy) {
-  const int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  const int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
   const int64_t total = (int64_t)M * N;
   if (e >= total) return;
   const int64_t m = e / N, n = e % N;
-  f32x4 a = *reinterpret_cast<const f32x4 *>(ws + e);
-  f32x4 b = *reinterpret_cast<const f32x4 *>(ws + e + 4);
-  // Partials 1 .. S-1 in groups of 8: a group's loads are all issued before
-  // its adds, which still run in s order (one memory round trip per group,
-  // not per partial).
-  for (int s0 = 1; s0 < S; s0 += 8) {
-    f32x4 pa[8], pb[8];
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += kCombineGroup) {
+    f32x4 p[kCombineGroup];
+    const float *q = ws + (int64_t)s0 * total + e;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (s0 + i < S) {
-        pa[i] = *reinterpret_cast<const f32x4 *>(ws + (int64_t)(s0 + i) * total + e);
-        pb[i] = *reinterpret_cast<const f32x4 *>(ws + (int64_t)(s0 + i) * total + e + 4);
-      }
-    }
+    for (int i = 0; i < kCombineGroup; ++i, q += total)
+      if (s0 + i < S) p[i] = *reinterpret_cast<const f32x4 *>(q);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (s0 + i < S) {
-        a = a + pa[i];
-        b = b + pb[i];
-      }
-    }
+    for (int i = 0; i < kCombineGroup; ++i)
+      if (s0 + i < S) a = (s0 + i == 0) ? p[i] : a + p[i];  // the fold starts from p_0 itself
   }
-  u32x4 o;
+  u32x2 o;
   o[0] = pack_bf16x2(a[0], a[1]);
   o[1] = pack_bf16x2(a[2], a[3]);
-  o[2] = pack_bf16x2(b[0], b[1]);
-  o[3] = pack_bf16x2(b[2], b[3]);
-  *reinterpret_cast<u32x4 *>(y + m * ldy + n) = o;
+  *reinterpret_cast<u32x2 *>(y + m * ldy + n) = o;
 }
 
 typedef void (*GemmKernel)(const uint16_t *, const uint16_t *, uint16_t *, int, int, int, int64_t,
@@ -866,7 +858,7 @@ extern "C" int bi_gemm_splitk(const uint16_t *x, const uint16_t *w, uint16_t *y,
                        dim3((unsigned)(tiles_m * tiles_n), (unsigned)split_k), dim3(kThreads), 0, s,
                        x, w, wsf, (int)M, (int)N, kc, ldx, ldw, (int)tiles_m, (int)tiles_n);
   if ((st = launch_status()) != BI_OK) return st;
-  const int64_t groups = (M * N / 8 + kThreads - 1) / kThreads;
+  const int64_t groups = (M * N / 4 + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(gemm_splitk_combine_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, wsf,
                      y, (int)M, (int)N, split_k, ldy);
   return launch_status();
