@@ -54,7 +54,10 @@ def test_rmsnorm_batch_invariance_prefix_permuted_reruns(bi):
     run = lambda xb: bi.bi_rmsnorm(xb, Wt, eps=workloads.EPS)
     perm = torch.from_numpy(synth.permutation(x.shape[0], c["perm_seed"]))
     probes = [0, 1, 6, 7, 127, 128, 2047, 4095, 8191] + list(range(200, 8192, 997))
-    batches = harness.prefix_and_permuted_batches(c["Ms"], x.shape[0], perm, "cuda")
+    # beyond the configured sizes: 3000 and 4096 run two and four rows per
+    # workgroup, 4097 one again, so rows meet every workgroup shape
+    batches = harness.prefix_and_permuted_batches(tuple(c["Ms"]) + (3000, 4096, 4097), x.shape[0],
+                                                  perm, "cuda")
     say("rmsnorm batch invariance")
     r = harness.batch_invariance(run, X, probes, batches)
     assert r["rows"] > 20 and r["diff_bits"] == 0, r
