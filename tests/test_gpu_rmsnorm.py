@@ -96,18 +96,22 @@ def test_rmsnorm_closed_forms(bi):
     assert np.all((z & 0x7FFF) == 0)
 
 
-def test_rmsnorm_in_place_and_strided(bi):
+@pytest.mark.parametrize("M", [33, 2500, 4096])
+def test_rmsnorm_in_place_and_strided(bi, M):
+    """In place and with row strides: the bits of the plain call.  M = 2500 and
+    4096 run two and four rows per workgroup (all of a workgroup's rows are
+    read before any is written)."""
     x, w = workloads.rmsnorm_inputs()
-    x = x[:33]
+    x = x[:M]
     ref = host_u16(bi.bi_rmsnorm(dev_bf16(x), dev_bf16(w), eps=workloads.EPS))
     X = dev_bf16(x)
     bi.bi_rmsnorm(X, dev_bf16(w), y=X, eps=workloads.EPS)
     assert np.array_equal(host_u16(X), ref)
     # strided input/output rows (ld > K)
-    big = np.zeros((33, 4096 + 64), np.uint16)
+    big = np.zeros((M, 4096 + 64), np.uint16)
     big[:, :4096] = x
     B = dev_bf16(big)
-    out = torch.zeros((33, 4096 + 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((M, 4096 + 128), dtype=torch.bfloat16, device="cuda")
     bi.bi_rmsnorm(B[:, :4096], dev_bf16(w), y=out[:, :4096], eps=workloads.EPS)
     o = host_u16(out)
     assert np.array_equal(o[:, :4096], ref)
