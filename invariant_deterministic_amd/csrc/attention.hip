@@ -70,13 +70,23 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   __shared__ __attribute__((aligned(1024))) uint16_t vs[VS * D];
-  __shared__ __attribute__((aligned(16))) float ps[GM][C];
+  // Score rows padded by 16 bytes so that rows of different heads start in
+  // different LDS banks.
+  __shared__ __attribute__((aligned(16))) float ps[GM][C + 4];
+  // Value rows in LDS: 16-byte unit u of row r sits at unit u ^ vswz(r), so
+  // the 16 rows one transposing read touches (rows 8q + j, j < 4, and the
+  // same + 4) fall on different banks instead of all on the same ones (a row
+  // is a whole number of bank widths long).
+  constexpr int VU = D / 8;  // 16-byte units of a value row
+  const auto vswz = [](int r) { return ((r & 3) | (((r >> 3) & 3) << 2)) & (VU - 1); };
 
   const int64_t row_stride = (int64_t)Hkv * D;  // elements between tokens
   const uint16_t *kseq = kc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D;
   const uint16_t *vseq = vc + ((int64_t)b * Tmax + t0) * row_stride + (int64_t)kh * D;
 
-  // Value rows of pass `pass` -> vs (row-major, D per row), direct to LDS.
+  // Value rows of pass `pass` -> vs (D per row, units swizzled by vswz),
+  // direct to LDS: lane l of an instruction fills unit position l % LPR of LDS
+  // row row0 + l / LPR, so it loads the row's unit (l % LPR) ^ vswz(row).
   // Rows at or past n load row n - 1 (in bounds, finite; their weight is 0).
   auto issue_v = [&](int pass) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -84,8 +94,10 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int row0 = (i * 4 + wv) * RPI;
-      const int t = min(pass * VS + row0 + lane / LPR, n - 1);
-      const int off = (int)(((int64_t)t * row_stride + (lane % LPR) * 8) * 2);
+      const int lrow = row0 + lane / LPR;
+      const int t = min(pass * VS + lrow, n - 1);
+      const int unit = (lane % LPR) ^ vswz(lrow);
+      const int off = (int)(((int64_t)t * row_stride + unit * 8) * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(vs + row0 * D), 16, off, 0, 0,
                                                kCpolNT);  // read once
     }
@@ -202,10 +214,12 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int d0 = (wv * CB + cb) * 16 + 4 * (jl & 3);
+        const int dlo = (((d0 >> 3) ^ vswz(vrow)) << 3) + (d0 & 7);
+        const int dhi = (((d0 >> 3) ^ vswz(vrow + 4)) << 3) + (d0 & 7);
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16 *)(vs + vrow * D + d0));
+            (__attribute__((address_space(3))) v4i16 *)(vs + vrow * D + dlo));
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16 *)(vs + (vrow + 4) * D + d0));
+            (__attribute__((address_space(3))) v4i16 *)(vs + (vrow + 4) * D + dhi));
         const v8i16 bb = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bb),
                                                            oacc[cb], 0, 0, 0);
