@@ -16,7 +16,8 @@
 // 2 * T_b * Hkv * D * 2 bytes of K and V per sequence.  Both are read as
 // whole 128-byte lines with the non-temporal hint: keys into registers, then
 // lane-permuted into the matrix-core layout; values as whole rows straight
-// into LDS, loaded while the scores are computed.
+// into LDS (16-byte units XOR-swizzled by row, so the transposing reads spread
+// over the banks), loaded while the scores are computed.
 //
 // Order of every output o[b][h][:] (G = H / Hkv query heads share key/value
 // head h / G; workgroup = 4 wavefronts):
