@@ -94,3 +94,57 @@ def test_graph_replays_reproduce_eager_bits(bi):
         assert torch.allclose(ref[4], out[4], rtol=1e-5, atol=1e-5), rep
         _chain(bi, X, G, W, A, B, *_buffers(X, W))   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_graph_decode_step_follows_device_lengths(bi):
+    """A decode step (RMSNorm over a batch of 4096 rows, which takes the
+    several-rows-per-workgroup path, then attention over a paged-free cache)
+    captured once; the sequence lengths live in device memory, so each replay
+    after the lengths grow in place must give the bits an eager call with those
+    lengths gives."""
+    M, K = 4096, 4096
+    X = dev_bf16(synth.normal_bf16((M, K), 9101))
+    G = dev_bf16(synth.normal_bf16((K,), 9102, mean=1.0, std=0.1))
+    B, H, Hkv, D, Tmax, split = 4, 32, 8, 128, 1100, 256
+    q = dev_bf16(synth.normal_bf16((B, H, D), 9103))
+    kc = dev_bf16(synth.normal_bf16((B, Tmax, Hkv, D), 9104))
+    vc = dev_bf16(synth.normal_bf16((B, Tmax, Hkv, D), 9105))
+    lens = torch.tensor([1, 255, 700, 1000], dtype=torch.int32, device=X.device)
+    need = bi.bi_decode_attention_workspace_bytes(B, H, Tmax, D, split)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=X.device)
+    Hn = torch.empty_like(X)
+    o = torch.empty((B, H, D), dtype=torch.bfloat16, device=X.device)
+
+    def step():
+        bi.bi_rmsnorm(X, G, y=Hn, eps=workloads.EPS)
+        bi.bi_decode_attention(q, kc, vc, lens, o=o, split_size=split, ws=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                                   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    prev = None
+    for rep in range(3):
+        lens.add_(rep * 33)                      # the cache grows between steps
+        torch.cuda.synchronize()
+        Hn.zero_()
+        o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"decode graph replay {rep} lens {lens.tolist()}")
+        got_h, got_o = Hn.clone(), o.clone()
+        step()                                   # eager with the same lengths
+        torch.cuda.synchronize()
+        assert torch.equal(got_h.view(torch.int16), Hn.view(torch.int16)), rep
+        assert torch.equal(got_o.view(torch.int16), o.view(torch.int16)), rep
+        assert int(got_o.view(torch.int16).ne(0).sum()) > 0, rep
+        if prev is not None:                     # the replay read the new lengths
+            assert not torch.equal(prev[0].view(torch.int16), got_o[0].view(torch.int16)), rep
+        prev = got_o
