@@ -55,6 +55,11 @@ def parse():
                              "splitk", "attention", "expand"])
     ap.add_argument("--iters", type=int, default=50, help="launches for --only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="report the step only (skip the metric's GEMM-over-M, RMSNorm, shrink, "
+                         "replay and 70B-stream parts)")
+    ap.add_argument("--replays", default=None,
+                    help="also run the shrink replay protocol over every configured M (JSONL to FILE)")
     ap.add_argument("--settle", type=float, default=2.5,
                     help="seconds of untimed steps before the warm-up steps, so the GPU "
                          "clocks leave their idle state (a few 1 ms steps do not); the "
@@ -110,23 +115,37 @@ def main():
         return
 
     # Probe rows: each computed alone through the whole chain, for the in-step
-    # bitwise check.
+    # bitwise check of every output the step writes.
     probes = sorted({0, 1, 255, 256, M // 2, M - 1} & set(range(M)))
-    solo_q = torch.empty((len(probes), N_Q), dtype=torch.bfloat16, device=dev)
-    solo_d = torch.empty((len(probes), K_MODEL), dtype=torch.bfloat16, device=dev)
+    P = len(probes)
+    solo = {"H": torch.empty((P, K_MODEL), dtype=torch.bfloat16, device=dev),
+            "Q": torch.empty((P, N_Q), dtype=torch.bfloat16, device=dev),
+            "KV": torch.empty((P, N_KV), dtype=torch.bfloat16, device=dev),
+            "U": torch.empty((P, N_UP), dtype=torch.bfloat16, device=dev),
+            "D": torch.empty((P, K_MODEL), dtype=torch.bfloat16, device=dev),
+            "L": torch.empty((P, R_LORA), dtype=torch.float32, device=dev),
+            "Lu": torch.empty((P, R_LORA), dtype=torch.float32, device=dev)}
     for i, p in enumerate(probes):
-        h1 = bi.bi_rmsnorm(X[p:p + 1], G, eps=eps)
-        bi.bi_gemm(h1, Wq, y=solo_q[i:i + 1])
-        u1 = bi.bi_gemm(h1, Wup)
-        bi.bi_gemm(u1, Wdown, y=solo_d[i:i + 1])
+        h1 = solo["H"][i:i + 1]
+        bi.bi_rmsnorm(X[p:p + 1], G, y=h1, eps=eps)
+        bi.bi_gemm(h1, Wq, y=solo["Q"][i:i + 1])
+        bi.bi_gemm(h1, Wkv, y=solo["KV"][i:i + 1])
+        bi.bi_gemm(h1, Wup, y=solo["U"][i:i + 1])
+        bi.bi_gemm(solo["U"][i:i + 1], Wdown, y=solo["D"][i:i + 1])
+        bi.bi_lora_shrink(h1, A, y=solo["L"][i:i + 1], split_k=8)
+        bi.bi_lora_shrink(h1, A, y=solo["Lu"][i:i + 1], split_k=1)
+    outs = {"H": H, "Q": Q, "KV": KV, "U": U, "D": D, "L": L, "Lu": Lu}
     probe_pos = torch.tensor(probes, dtype=torch.int64, device=dev)
-    probe_ids = torch.arange(len(probes), dtype=torch.int64, device=dev)
-    counts_q = torch.zeros((len(probes), 2), dtype=torch.int64, device=dev)
-    counts_d = torch.zeros((len(probes), 2), dtype=torch.int64, device=dev)
+    probe_ids = torch.arange(P, dtype=torch.int64, device=dev)
+    # one counts slot per output and per step (the gate step, then each timed
+    # step), so that every timed step's comparison is kept, not just the last
+    nslots = 1 + args.steps
+    counts = torch.zeros((nslots, len(outs), P, 2), dtype=torch.int64, device=dev)
+    scratch_counts = torch.zeros((len(outs), P, 2), dtype=torch.int64, device=dev)
 
     ev_pairs = []
 
-    def step(timed: bool):
+    def step(timed: bool, slot=None):
         bi.bi_rmsnorm(X, G, y=H, eps=eps)
         for w, y, inp in ((Wq, Q, H), (Wkv, KV, H), (Wup, U, H), (Wdown, D, U)):
             big = w.shape[0] >= 4096
@@ -141,15 +160,17 @@ def main():
         bi.bi_lora_shrink(H, A, y=L, split_k=8)
         bi.bi_lora_shrink(H, A, y=Lu, split_k=1)
         bi.bi_lora_shrink_atomic(H, A, y=La, split_k=8)
-        bi.bi_row_bitdiff(Q, solo_q, probe_pos, probe_ids, counts=counts_q, check_rows=False)
-        bi.bi_row_bitdiff(D, solo_d, probe_pos, probe_ids, counts=counts_d, check_rows=False)
+        cs = counts[slot] if slot is not None else scratch_counts
+        for j, name in enumerate(outs):
+            bi.bi_row_bitdiff(outs[name], solo[name], probe_pos, probe_ids, counts=cs[j],
+                              check_rows=False)
 
     # Gate before timing: the path must be batch-invariant on this input.
-    step(False)
+    step(False, slot=0)
     torch.cuda.synchronize()
-    gate_bits = int(counts_q[:, 0].sum()) + int(counts_d[:, 0].sum())
-    if gate_bits:
-        print(json.dumps({"error": "batch-invariance gate failed", "diff_bits": gate_bits}))
+    gate = {name: int(counts[0, j, :, 0].sum()) for j, name in enumerate(outs)}
+    if any(gate.values()):
+        print(json.dumps({"error": "batch-invariance gate failed", "diff_bits": gate}))
         sys.exit(1)
 
     # Untimed: let the clocks ramp from idle (measured: with only a handful of
@@ -170,8 +191,8 @@ def main():
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(args.steps):
-        step(True)
+    for i in range(args.steps):
+        step(True, slot=1 + i)
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -193,7 +214,10 @@ def main():
                 "avg_launch_us": round(avg_ms * 1e3, 2),
                 "flop_per_launch": avg_flop}
 
-    bits_after = int(counts_q[:, 0].sum()) + int(counts_d[:, 0].sum())
+    timed_bits = counts[1:, :, :, 0].sum(dim=(0, 2)).tolist()
+    invariance = {"probe_rows": P, "outputs": list(outs),
+                  "timed_steps_checked": args.steps,
+                  "diff_bits_timed_steps": {n: int(b) for n, b in zip(outs, timed_bits)}}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -203,16 +227,209 @@ def main():
                    "N": [N_Q, N_KV, N_UP], "down_proj": [N_UP, K_MODEL], "lora_rank": R_LORA,
                    "lora_split_k": 8, "parallelism": "single-gpu"},
         "roofline": roofline,
-        "invariance": {"probe_rows": len(probes), "diff_bits_last_step": bits_after},
+        "invariance": invariance,
         "settle": {"seconds": args.settle, "untimed_steps": settle_steps},
         "clock": clk.summary(achieved),
     }
+    if not args.step_only:
+        print("# metric parts: GEMM over M, RMSNorm, shrink, replays, 70B stream",
+              file=sys.stderr, flush=True)
+        out.update(metric_parts(bi, torch, dev, H, Wq, Wkv, Wup, Wdown, A, G, eps))
+        invariance.update(out.pop("replays"))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, g, ws_h, a, eps)
     if args.sweep:
         out["sweep_file"] = args.sweep
         sweep(args.sweep, bi, torch, dev, to_dev)
+    if args.replays:
+        replay_table(args.replays, bi, torch, dev, to_dev)
     print(json.dumps(out), flush=True)
+
+
+GiB = 1 << 30
+
+
+def _copies(nbytes: int) -> int:
+    """Copies of a buffer set that together touch at least 1 GiB, so the
+    256 MB last-level cache cannot serve a rotated loop."""
+    return max(1, min(64, -(-GiB // max(1, nbytes))))
+
+
+def _geomean(v):
+    import math
+    return math.exp(sum(math.log(x) for x in v) / len(v))
+
+
+def metric_parts(bi, torch, dev, H, Wq, Wkv, Wup, Wdown, A, G, eps):
+    """The parts of the headline metric beyond the step, each graph-timed:
+    the batch-invariant GEMM over M at every projection shape, RMSNorm over
+    rotated copies at the configured batch sizes, the three shrink variants at
+    M = 4096 with the pages' two latency ratios, the replay variation of the
+    atomic control against the deterministic split, and the Llama-3-70B
+    dynamic-batch stream."""
+    from invariant_deterministic_amd import harness, synth, workloads
+    res = {}
+
+    # GEMM over M (compute-bound from M ~ 350: the inputs need no rotation)
+    xp = {4096: synth.device_normal_bf16((8192, 4096), 3101),
+          14336: synth.device_normal_bf16((8192, 14336), 3102)}
+    shapes = (("q", Wq), ("kv", Wkv), ("up", Wup), ("down", Wdown))
+    g_out = {"kernel": "bi_gemm (one tile configuration per (N, K))", "peak_tflops": PEAK_BF16_TFLOPS,
+             "shapes": {}}
+    fracs = []
+    for name, W in shapes:
+        N, K = W.shape
+        y = torch.empty((8192, N), dtype=torch.bfloat16, device=dev)
+        pts = {}
+        for M in (2048, 4096, 8192):
+            xm, ym = xp[K][:M], y[:M]
+            ms = _time_loop(torch, lambda i: bi.bi_gemm(xm, W, y=ym), 20)
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            pts[str(M)] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1),
+                           "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+            fracs.append(tf / PEAK_BF16_TFLOPS)
+        gm = _geomean([v["frac"] for v in pts.values()])
+        g_out["shapes"][name] = {"K": K, "N": N, "config": bi.bi_gemm_config_id(N, K), "M": pts,
+                                 "geomean_frac": round(gm, 4)}
+        print(f"# gemm over M {name}: " + ", ".join(f"M={m} {v['frac']:.3f}" for m, v in pts.items()),
+              file=sys.stderr, flush=True)
+        del y
+    g_out["geomean_frac_all"] = round(_geomean(fracs), 4)
+    res["gemm_over_m"] = g_out
+    del xp
+
+    # RMSNorm, K = 4096, inputs and outputs rotated over >= 1 GiB
+    K = 4096
+    r_out = {"K": K, "bytes": "4*M*K + 2*K", "peak_gbs": PEAK_HBM_GBS, "M": {}}
+    for M in (1, 7, 128, 2048, 8192):
+        c = _copies(4 * M * K)
+        xs = [synth.device_normal_bf16((M, K), 2100 + i) for i in range(c)]
+        ys = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(c)]
+        ms = _time_loop(torch, lambda i: bi.bi_rmsnorm(xs[i % c], G, y=ys[i % c], eps=eps), 4 * c)
+        gbs = (4.0 * M * K + 2 * K) / (ms * 1e-3) / 1e9
+        r_out["M"][str(M)] = {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                              "frac": round(gbs / PEAK_HBM_GBS, 4), "rotating_copies": c}
+        del xs, ys
+    print(f"# rmsnorm: " + ", ".join(f"M={m} {v['frac']:.3f}" for m, v in r_out["M"].items()),
+          file=sys.stderr, flush=True)
+    res["rmsnorm"] = r_out
+
+    # LoRA shrink at M = 4096, x rotated over >= 1 GiB
+    M, K, R = 4096, 4096, R_LORA
+    c = _copies(2 * M * K)
+    xs = [synth.device_normal_bf16((M, K), 4100 + i) for i in range(c)]
+    y = torch.empty((M, R), dtype=torch.float32, device=dev)
+    ws = torch.empty(bi.bi_lora_shrink_workspace_bytes(M, R, 8), dtype=torch.uint8, device=dev)
+    by = 2.0 * M * K + 2 * R * K + 4 * M * R
+    s_out = {"M": M, "K": K, "R": R, "bytes": "2*M*K + 2*R*K + 4*M*R", "peak_gbs": PEAK_HBM_GBS,
+             "rotating_copies": c, "variants": {}}
+    t = {}
+    for name, fn in (("det8", lambda i: bi.bi_lora_shrink(xs[i % c], A, y=y, split_k=8)),
+                     ("det8_two_pass", lambda i: bi.bi_lora_shrink_two_pass(xs[i % c], A, y=y,
+                                                                          split_k=8, ws=ws)),
+                     ("atomic8", lambda i: bi.bi_lora_shrink_atomic(xs[i % c], A, y=y, split_k=8)),
+                     ("unsplit", lambda i: bi.bi_lora_shrink(xs[i % c], A, y=y, split_k=1))):
+        ms = _time_loop(torch, fn, 4 * c)
+        t[name] = ms
+        gbs = by / (ms * 1e-3) / 1e9
+        s_out["variants"][name] = {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                                   "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    s_out["det8_latency_over_atomic8"] = round(t["det8"] / t["atomic8"], 4)
+    s_out["det8_speedup_over_unsplit"] = round(t["unsplit"] / t["det8"] - 1.0, 4)
+    s_out["pages"] = {"det8_over_atomic8_added_latency": "+1.02..2.62 %",
+                      "det8_speedup_over_unsplit": "16.8..21.1 %", "hardware": "not stated"}
+    print(f"# shrink M=4096: " + ", ".join(f"{k} {v['us']} us" for k, v in s_out["variants"].items()),
+          file=sys.stderr, flush=True)
+    res["shrink"] = s_out
+    del xs
+
+    # Identical-input replay at M = 4096: the atomic control against the
+    # deterministic split (a replay differs when any output bit differs from
+    # replay 0)
+    Hm = H[:M]
+    rep = {}
+    for name, fn in (("det8", lambda xb: bi.bi_lora_shrink(xb, A, y=y, split_k=8)),
+                     ("atomic8", lambda xb: bi.bi_lora_shrink_atomic(xb, A, y=y, split_k=8))):
+        r = harness.replay_variation(fn, Hm, 201)
+        rep[name] = {"replays": r["replays"], "differing": r["differing"],
+                     "frac_differing": round(r["frac_differing"], 4),
+                     "diff_elems": r["diff_elems"], "elems_per_replay": r["elems_per_replay"]}
+    res["replays"] = {"shrink_replays_m4096": rep}
+    print(f"# replays M=4096: atomic8 {rep['atomic8']['differing']}/200, det8 "
+          f"{rep['det8']['differing']}/200", file=sys.stderr, flush=True)
+
+    # Llama-3-70B MLP shape under the dynamic-batch stream: 200 batches,
+    # M ~ U{1..4096}, 8 probe rows at random positions, each checked bitwise
+    # against its solo output
+    cfg = workloads.LLAMA70B
+    probes, batches = workloads.llama70b_stream()
+    Xp = synth.device_normal_bf16((cfg["pool_rows"], cfg["K"]), 5101)
+    W70 = synth.device_normal_bf16((cfg["N"], cfg["K"]), 5102, std=cfg["w_std"])
+    solo = torch.cat([bi.bi_gemm(Xp[int(p):int(p) + 1], W70) for p in probes], dim=0)
+    ybuf = torch.empty((cfg["m_max"], cfg["N"]), dtype=torch.bfloat16, device=dev)
+    xbs, checks = [], []
+    for b in batches:
+        idx = torch.from_numpy(b["rows"]).to(dev)
+        xbs.append(Xp.index_select(0, idx))
+        present = [q for q in range(len(probes)) if b["probe_pos"][q] >= 0]
+        checks.append((torch.tensor([int(b["probe_pos"][q]) for q in present], dtype=torch.int64,
+                                    device=dev),
+                       torch.tensor(present, dtype=torch.int64, device=dev)))
+    cnt = torch.zeros((len(batches), len(probes), 2), dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i, xb in enumerate(xbs):
+        bi.bi_gemm(xb, W70, y=ybuf[:xb.shape[0]])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    for i, xb in enumerate(xbs):  # the comparison, outside the timed loop
+        bi.bi_gemm(xb, W70, y=ybuf[:xb.shape[0]])
+        pos, pid = checks[i]
+        if pos.numel():
+            bi.bi_row_bitdiff(ybuf, solo, pos, pid, counts=cnt[i, :pos.numel()], check_rows=False)
+    torch.cuda.synchronize()
+    ms_all = [xb.shape[0] for xb in xbs]
+    fl = sum(2.0 * m * cfg["N"] * cfg["K"] for m in ms_all)
+    res["stream70b"] = {"K": cfg["K"], "N": cfg["N"], "batches": len(xbs), "M_min": min(ms_all),
+                        "M_max": max(ms_all), "rows": sum(ms_all), "ms": round(ms, 3),
+                        "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                        "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "probe_rows_checked": int(sum(c[0].numel() for c in checks)),
+                        "probe_diff_bits": int(cnt[:, :, 0].sum())}
+    print(f"# 70b stream: {res['stream70b']['tflops']} TFLOP/s, "
+          f"{res['stream70b']['probe_diff_bits']} differing bits", file=sys.stderr, flush=True)
+    return res
+
+
+def replay_table(path, bi, torch, dev, to_dev):
+    """The replay protocol of the LoRA shrink over every configured M: each
+    variant replayed 1000 times on the same buffers; one JSON line per
+    (variant, M) into ``path``."""
+    from invariant_deterministic_amd import harness, workloads
+    c = workloads.LORA
+    x, a = workloads.lora_inputs()
+    X, A = to_dev(x), to_dev(a)
+    recs = []
+    for M in c["Ms"]:
+        Xm = X[:M]
+        y = torch.empty((M, 16), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(16, bi.bi_lora_shrink_workspace_bytes(M, 16, 8)), dtype=torch.uint8,
+                         device=dev)
+        for v, fn in (("det8", lambda xb: bi.bi_lora_shrink(xb, A, y=y, split_k=8)),
+                      ("det8_two_pass", lambda xb: bi.bi_lora_shrink_two_pass(xb, A, y=y, split_k=8,
+                                                                              ws=ws)),
+                      ("unsplit", lambda xb: bi.bi_lora_shrink(xb, A, y=y, split_k=1)),
+                      ("atomic8", lambda xb: bi.bi_lora_shrink_atomic(xb, A, y=y, split_k=8))):
+            r = harness.replay_variation(fn, Xm, c["replays"])
+            r.update(variant=v, M=M)
+            recs.append(r)
+            print(f"# replays {v} M={M}: {r['differing']}/{r['comparisons']} differ, "
+                  f"{r['diff_elems']} elements", file=sys.stderr, flush=True)
+    with open(path, "w") as f:
+        for r in recs:
+            f.write(json.dumps(r) + "\n")
 
 
 class ClockSampler:

@@ -112,8 +112,39 @@ int bi_gemm(const uint16_t *x, const uint16_t *w, uint16_t *y,
  * bi_gemm_config_id -- the tile configuration bi_gemm uses for (N, K), or -1
  * if (N, K) is not supported.  It takes no M on purpose: the configuration,
  * and with it every output's reduction order, cannot depend on the batch size.
+ *
+ * Defined by: "Cómo superar la no determinación en la inferencia de LLM",
+ * section "Multiplicación de matrices (matmul)": one kernel configuration
+ * forced for every batch size.
  */
 int bi_gemm_config_id(int64_t N, int64_t K);
+
+/*
+ * bi_gemm_launch_plan -- what bi_gemm(M, N, K) would launch, without launching
+ * anything: a static check that the batch size reaches nothing but the number
+ * of workgroups.
+ *
+ * Defined by: "God Does Not Play Dice: Enforcing Batch Invariance in Agentic
+ * Kernel Generation", abstract (a static, contract-guided check of what a
+ * kernel's reduction depends on, beside the dynamic bitwise one), and "Cómo
+ * superar la no determinación en la inferencia de LLM", section
+ * "Multiplicación de matrices (matmul)" (one configuration for every batch
+ * size).
+ *
+ *   plan   host int64_t[7], written on BI_OK:
+ *          [0] configuration (= bi_gemm_config_id(N, K)),
+ *          [1] kernel id (which compiled kernel runs),
+ *          [2] tile rows (of M), [3] tile columns (of N),
+ *          [4] k per LDS stage (32 or 64; the 16-k matrix-core steps are the
+ *              same either way), [5] threads per workgroup,
+ *          [6] workgroups = ceil(M / tile rows) * ceil(N / tile columns)
+ *              (0 when M == 0).
+ *   Entries [0]..[5] depend on (N, K) only.  bi_gemm builds its launch from
+ *   the same host function.
+ * Returns BI_ERR_NULL for a NULL plan, BI_ERR_SHAPE when M < 0 or (N, K) is
+ * not supported (see bi_gemm_config_id); touches no device.
+ */
+int bi_gemm_launch_plan(int64_t M, int64_t N, int64_t K, int64_t *plan);
 
 /*
  * bi_gemm_num_configs / bi_gemm_with_config -- tuning and verification hooks.

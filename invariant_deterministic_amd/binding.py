@@ -42,6 +42,7 @@ _lib_rmsnorm = _sig("bi_rmsnorm", [_p, _p, _p, _i64, _i64, _i64, _i64, ctypes.c_
 _lib_gemm = _sig("bi_gemm", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p])
 _lib_gemm_config_id = _sig("bi_gemm_config_id", [_i64, _i64])
 _lib_gemm_num_configs = _sig("bi_gemm_num_configs", [])
+_lib_gemm_launch_plan = _sig("bi_gemm_launch_plan", [_i64, _i64, _i64, _p])
 _lib_gemm_fill = _sig("bi_gemm_fill", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p])
 _lib_gemm_fill_config_id = _sig("bi_gemm_fill_config_id", [_i64, _i64, _i64])
 _lib_gemm_with_config = _sig("bi_gemm_with_config",
@@ -72,7 +73,7 @@ _lib_row_bitdiff = _sig("bi_row_bitdiff", [_p, _i64, _p, _p, _i64, _p, _i64, _i6
 
 BI_OK = 0
 EXPORTS = ("bi_abi_version", "bi_status_str", "bi_rmsnorm", "bi_gemm", "bi_gemm_config_id",
-           "bi_gemm_num_configs", "bi_gemm_with_config", "bi_gemm_fill", "bi_gemm_fill_config_id",
+           "bi_gemm_num_configs", "bi_gemm_with_config", "bi_gemm_launch_plan", "bi_gemm_fill", "bi_gemm_fill_config_id",
            "bi_gemm_splitk",
            "bi_gemm_splitk_workspace_bytes", "bi_gemm_splitk_for", "bi_gemm_mswitch_control", "bi_lora_shrink_workspace_bytes",
            "bi_lora_shrink", "bi_lora_shrink_two_pass", "bi_lora_shrink_atomic", "bi_row_bitdiff",
@@ -109,6 +110,25 @@ def _stream(stream) -> int | None:
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
 
 
+def _dims(t, name: str, ndim: int = 2) -> tuple:
+    """Shape of ``t`` after checking it is a torch tensor of ``ndim`` dimensions.
+    Shapes are checked before anything about the device, so a wrong shape is
+    reported the same way with or without a GPU, and before any launch."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _want(t, shape: tuple, name: str):
+    """Raise unless tensor ``t`` has exactly ``shape``."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def _mat(t: torch.Tensor, name: str, dtypes) -> tuple[int, int]:
     """Validate a row-major device matrix; return (data_ptr, row stride)."""
     if not isinstance(t, torch.Tensor):
@@ -135,32 +155,39 @@ def bi_status_str(status: int) -> str:
 def bi_rmsnorm(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,
                eps: float = 1e-6, stream=None) -> torch.Tensor:
     """y = RMSNorm(x) * w, one workgroup per row (see bi.h)."""
-    M, K = x.shape
-    if y is None:
+    M, K = _dims(x, "x")
+    _want(w, (K,), "w")
+    if y is not None:
+        _want(y, (M, K), "y")
+    else:
         y = torch.empty((M, K), dtype=x.dtype, device=x.device)
     px, ldx = _mat(x, "x", _BF16_LIKE)
     pw, _ = _mat(w, "w", _BF16_LIKE)
     py, ldy = _mat(y, "y", _BF16_LIKE)
-    if w.numel() != K or tuple(y.shape) != (M, K):
-        raise ValueError("shape mismatch")
     _check(_lib_rmsnorm(px, pw, py, M, K, ldx, ldy, float(eps), _stream(stream)), "bi_rmsnorm")
     return y
+
+
+def _gemm_shapes(x, w, y):
+    """(M, N, K, y) for x [M, K] . w [N, K]^T, allocating y [M, N] if None."""
+    M, K = _dims(x, "x")
+    N, Kw = _dims(w, "w")
+    if Kw != K:
+        raise ValueError(f"x has K = {K} columns but w has {Kw}")
+    if y is not None:
+        _want(y, (M, N), "y")
+    else:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    return M, N, K, y
 
 
 def bi_gemm(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,
             stream=None) -> torch.Tensor:
     """y[M, N] = x[M, K] . w[N, K]^T in bf16 with fp32 accumulation (see bi.h)."""
-    M, K = x.shape
-    N = w.shape[0]
-    if w.shape[1] != K:
-        raise ValueError("x and w disagree on K")
-    if y is None:
-        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    M, N, K, y = _gemm_shapes(x, w, y)
     px, ldx = _mat(x, "x", _BF16_LIKE)
     pw, ldw = _mat(w, "w", _BF16_LIKE)
     py, ldy = _mat(y, "y", _BF16_LIKE)
-    if tuple(y.shape) != (M, N):
-        raise ValueError("y has the wrong shape")
     _check(_lib_gemm(px, pw, py, M, N, K, ldx, ldw, ldy, _stream(stream)), "bi_gemm")
     return y
 
@@ -173,12 +200,19 @@ def bi_gemm_num_configs() -> int:
     return int(_lib_gemm_num_configs())
 
 
+PLAN_FIELDS = ("config", "kernel", "tile_m", "tile_n", "k_stage", "threads", "workgroups")
+
+
+def bi_gemm_launch_plan(M: int, N: int, K: int) -> dict:
+    """What bi_gemm(M, N, K) would launch (host only; see bi.h)."""
+    buf = (ctypes.c_int64 * len(PLAN_FIELDS))()
+    _check(_lib_gemm_launch_plan(M, N, K, ctypes.cast(buf, _p)), "bi_gemm_launch_plan")
+    return dict(zip(PLAN_FIELDS, (int(v) for v in buf)))
+
+
 def bi_gemm_with_config(config: int, x: torch.Tensor, w: torch.Tensor,
                         y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    M, K = x.shape
-    N = w.shape[0]
-    if y is None:
-        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    M, N, K, y = _gemm_shapes(x, w, y)
     px, ldx = _mat(x, "x", _BF16_LIKE)
     pw, ldw = _mat(w, "w", _BF16_LIKE)
     py, ldy = _mat(y, "y", _BF16_LIKE)
@@ -190,15 +224,10 @@ def bi_gemm_with_config(config: int, x: torch.Tensor, w: torch.Tensor,
 def bi_gemm_fill(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,
                  stream=None) -> torch.Tensor:
     """bi_gemm with the tile picked per call to fill the chip; same bits (see bi.h)."""
-    M, K = x.shape
-    N = w.shape[0]
-    if y is None:
-        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    M, N, K, y = _gemm_shapes(x, w, y)
     px, ldx = _mat(x, "x", _BF16_LIKE)
     pw, ldw = _mat(w, "w", _BF16_LIKE)
     py, ldy = _mat(y, "y", _BF16_LIKE)
-    if tuple(y.shape) != (M, N):
-        raise ValueError("y has the wrong shape")
     _check(_lib_gemm_fill(px, pw, py, M, N, K, ldx, ldw, ldy, _stream(stream)), "bi_gemm_fill")
     return y
 
@@ -216,10 +245,9 @@ def bi_gemm_splitk_for(N: int, K: int) -> int:
 
 
 def _gemm_ws_call(fn, name, x, w, y, split_k, ws, stream):
-    M, K = x.shape
-    N = w.shape[0]
-    if y is None:
-        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    M, N, K, y = _gemm_shapes(x, w, y)
+    if ws is not None and not isinstance(ws, torch.Tensor):
+        raise TypeError("ws must be a torch.Tensor")
     if ws is None:
         need = bi_gemm_splitk_workspace_bytes(M, N, split_k if split_k else
                                               max(1, bi_gemm_splitk_for(N, K)))
@@ -270,11 +298,23 @@ def bi_lora_shrink_two_pass(x: torch.Tensor, a: torch.Tensor, y: torch.Tensor | 
                    True)
 
 
-def _shrink(fn, name, x, a, y, split_k, ws, stream, need_ws):
-    M, K = x.shape
-    R = a.shape[0]
-    if y is None:
+def _shrink_shapes(x, a, y):
+    """(M, K, R, y) for x [M, K] . a [R, K]^T, allocating y [M, R] fp32 if None."""
+    M, K = _dims(x, "x")
+    R, Ka = _dims(a, "a")
+    if Ka != K:
+        raise ValueError(f"x has K = {K} columns but a has {Ka}")
+    if y is not None:
+        _want(y, (M, R), "y")
+    else:
         y = torch.empty((M, R), dtype=torch.float32, device=x.device)
+    return M, K, R, y
+
+
+def _shrink(fn, name, x, a, y, split_k, ws, stream, need_ws):
+    M, K, R, y = _shrink_shapes(x, a, y)
+    if ws is not None and not isinstance(ws, torch.Tensor):
+        raise TypeError("ws must be a torch.Tensor")
     need = bi_lora_shrink_workspace_bytes(M, R, split_k)
     if ws is None and need > 0 and need_ws:
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -290,10 +330,7 @@ def _shrink(fn, name, x, a, y, split_k, ws, stream, need_ws):
 def bi_lora_shrink_atomic(x: torch.Tensor, a: torch.Tensor, y: torch.Tensor | None = None,
                           split_k: int = 8, stream=None) -> torch.Tensor:
     """CONTROL ONLY: split-K shrink combined with fp32 atomics (nondeterministic)."""
-    M, K = x.shape
-    R = a.shape[0]
-    if y is None:
-        y = torch.empty((M, R), dtype=torch.float32, device=x.device)
+    M, K, R, y = _shrink_shapes(x, a, y)
     px, ldx = _mat(x, "x", _BF16_LIKE)
     pa, lda = _mat(a, "a", _BF16_LIKE)
     py, ldy = _mat(y, "y", (torch.float32,))
@@ -328,6 +365,10 @@ def bi_row_bitdiff(a: torch.Tensor, b: torch.Tensor, a_rows: torch.Tensor | None
         raise IndexError("more rows compared than present")
     if counts is None:
         counts = torch.empty((nrows, 2), dtype=torch.int64, device=a.device)
+    else:
+        _want(counts, (nrows, 2), "counts")
+        if counts.dtype != torch.int64 or not counts.is_contiguous():
+            raise ValueError("counts must be a contiguous int64 [nrows, 2] tensor")
     pa, lda = _mat(a, "a", (a.dtype,))
     pb, ldb = _mat(b, "b", (b.dtype,))
     _check(_lib_row_bitdiff(pa, lda, a_rows.data_ptr() if a_rows is not None else None,
@@ -346,10 +387,13 @@ def bi_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
                         ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Batch-invariant decode attention (see bi.h).  q [B, H, D]; caches
     [B, Tmax, Hkv, D]; lens int32 [B] on the device."""
-    B, H, D = q.shape
-    Bk, Tmax, Hkv, Dk = k_cache.shape
+    B, H, D = _dims(q, "q", 3)
+    Bk, Tmax, Hkv, Dk = _dims(k_cache, "k_cache", 4)
     if tuple(v_cache.shape) != tuple(k_cache.shape) or Bk != B or Dk != D:
         raise ValueError("cache shapes do not match q")
+    _want(lens, (B,), "lens")
+    if o is not None:
+        _want(o, (B, H, D), "o")
     for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         if not t.is_cuda or t.dtype not in _BF16_LIKE or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous bf16 device tensor")
@@ -372,9 +416,15 @@ def bi_lora_expand(l: torch.Tensor, b: torch.Tensor, base: torch.Tensor | None =
                    y: torch.Tensor | None = None, scale: float = 1.0,
                    stream=None) -> torch.Tensor:
     """y = bf16(base + scale * l . b^T), l fp32 [M, R], b bf16 [N, R] (see bi.h)."""
-    M, R = l.shape
-    N = b.shape[0]
-    if y is None:
+    M, R = _dims(l, "l")
+    N, Rb = _dims(b, "b")
+    if Rb != R:
+        raise ValueError(f"l has R = {R} columns but b has {Rb}")
+    if base is not None:
+        _want(base, (M, N), "base")
+    if y is not None:
+        _want(y, (M, N), "y")
+    else:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=l.device)
     pl, ldl = _mat(l, "l", (torch.float32,))
     pb, ldb = _mat(b, "b", _BF16_LIKE)
@@ -391,10 +441,18 @@ def bi_lora_shrink_expand(x: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
                           stream=None) -> torch.Tensor:
     """y = bf16(base + scale * shrink(x, a) . b^T) in one launch (see bi.h); l, if
     given (fp32 [M, R]), receives the shrink output."""
-    M, K = x.shape
-    R = a.shape[0]
-    N = b.shape[0]
-    if y is None:
+    M, K = _dims(x, "x")
+    R, Ka = _dims(a, "a")
+    N, Rb = _dims(b, "b")
+    if Ka != K or Rb != R:
+        raise ValueError(f"x [M, {K}], a [{R}, {Ka}] and b [N, {Rb}] disagree on K or R")
+    if base is not None:
+        _want(base, (M, N), "base")
+    if l is not None:
+        _want(l, (M, R), "l")
+    if y is not None:
+        _want(y, (M, N), "y")
+    else:
         y = torch.empty((M, N), dtype=x.dtype, device=x.device)
     px, ldx = _mat(x, "x", _BF16_LIKE)
     pa, lda = _mat(a, "a", _BF16_LIKE)
@@ -402,9 +460,6 @@ def bi_lora_shrink_expand(x: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
     py, ldy = _mat(y, "y", _BF16_LIKE)
     pbase, ldbase = _mat(base, "base", _BF16_LIKE) if base is not None else (None, N)
     pl, ldl = _mat(l, "l", (torch.float32,)) if l is not None else (None, R)
-    if tuple(y.shape) != (M, N) or (base is not None and tuple(base.shape) != (M, N)) or \
-            (l is not None and tuple(l.shape) != (M, R)) or b.shape[1] != R:
-        raise ValueError("shape mismatch")
     _check(_lib_shrink_expand(px, pa, pb, pbase, py, pl, M, K, N, R, ldx, lda, ldb, ldbase, ldy,
                               ldl, float(scale), split_k, _stream(stream)), "bi_lora_shrink_expand")
     return y

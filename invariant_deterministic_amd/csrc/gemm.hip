@@ -756,15 +756,28 @@ int validate(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64
   return BI_OK;
 }
 
+// Everything a launch of configuration cfg depends on.  M enters only the
+// number of tile rows (how many workgroups run), never the kernel, its tile or
+// its K stage.
+struct Plan {
+  int cfg, bm, bn, kstage;
+  int64_t tiles_m, tiles_n;
+  GemmKernel kern;
+};
+Plan plan_for(int cfg, int64_t M, int64_t N, int64_t K) {
+  const CfgEntry &c = kConfigs[cfg];
+  const bool wide = c.wide && K % BK2 == 0;
+  return Plan{cfg, c.bm, c.bn, wide ? BK2 : BK, (M + c.bm - 1) / c.bm, (N + c.bn - 1) / c.bn,
+              wide ? c.wide : c.kernel};
+}
+
 int launch(int cfg, const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t N,
            int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, void *stream) {
-  const CfgEntry &c = kConfigs[cfg];
-  const int64_t tiles_m = (M + c.bm - 1) / c.bm, tiles_n = (N + c.bn - 1) / c.bn;
-  if (tiles_m * tiles_n > 0x7FFFFFFF) return BI_ERR_SHAPE;
-  const GemmKernel kern = (c.wide && K % BK2 == 0) ? c.wide : c.kernel;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0,
+  const Plan p = plan_for(cfg, M, N, K);
+  if (p.tiles_m * p.tiles_n > 0x7FFFFFFF) return BI_ERR_SHAPE;
+  hipLaunchKernelGGL(p.kern, dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(kThreads), 0,
                      (hipStream_t)stream, x, w, y, (int)M, (int)N, (int)K, ldx, ldw, ldy,
-                     (int)tiles_m, (int)tiles_n);
+                     (int)p.tiles_m, (int)p.tiles_n);
   return launch_status();
 }
 
@@ -783,6 +796,27 @@ extern "C" int bi_gemm(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_
   const int st = validate(x, w, y, M, N, K, ldx, ldw, ldy);
   if (st != BI_OK || M == 0) return st;
   return launch(config_for(N, K), x, w, y, M, N, K, ldx, ldw, ldy, stream);
+}
+
+extern "C" int bi_gemm_launch_plan(int64_t M, int64_t N, int64_t K, int64_t *plan) {
+  if (!plan) return BI_ERR_NULL;
+  const int cfg = bi_gemm_config_id(N, K);
+  if (M < 0 || cfg < 0) return BI_ERR_SHAPE;
+  // the same function bi_gemm's launch() builds its launch from
+  const Plan p = plan_for(cfg, M, N, K);
+  int64_t kid = -1;
+  for (int c = 0; c < kNumConfigs; ++c) {
+    if (p.kern == kConfigs[c].kernel) kid = 2 * c;
+    if (p.kern == kConfigs[c].wide) kid = 2 * c + 1;
+  }
+  plan[0] = p.cfg;
+  plan[1] = kid;
+  plan[2] = p.bm;
+  plan[3] = p.bn;
+  plan[4] = p.kstage;
+  plan[5] = kThreads;
+  plan[6] = M == 0 ? 0 : p.tiles_m * p.tiles_n;
+  return BI_OK;
 }
 
 extern "C" int bi_gemm_num_configs(void) { return kNumConfigs; }
@@ -829,25 +863,28 @@ extern "C" size_t bi_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int split
   return (b + 255u) & ~(size_t)255u;
 }
 
-extern "C" int bi_gemm_splitk(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M,
-                              int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
-                              int split_k, void *ws, size_t ws_bytes, void *stream) {
-  int st = validate(x, w, y, M, N, K, ldx, ldw, ldy);
+namespace bi {
+namespace {
+
+// Checks of bi_gemm_splitk's operands other than the workspace.
+int splitk_validate(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t N,
+                    int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, int split_k) {
+  const int st = validate(x, w, y, M, N, K, ldx, ldw, ldy);
   if (st != BI_OK) return st;
   if (split_k < 1 || split_k > 64) return BI_ERR_UNSUPPORTED;
   if (K % ((int64_t)split_k * BK)) return BI_ERR_SHAPE;
-  if (M == 0) return BI_OK;
-  if (!ws) return BI_ERR_NULL;
-  if (ws_bytes < bi_gemm_splitk_workspace_bytes(M, N, split_k)) return BI_ERR_WORKSPACE;
-  if (!aligned16(ws)) return BI_ERR_ALIGN;
-  const Span sw{(uintptr_t)ws, (uintptr_t)ws + (uintptr_t)(split_k * M * N * 4)};
-  if (overlap(sw, span_of(y, M, N, ldy, 2)) || overlap(sw, span_of(x, M, K, ldx, 2)) ||
-      overlap(sw, span_of(w, N, K, ldw, 2)))
-    return BI_ERR_ALIAS;
+  if (M > 0 && ((M + kSplitBM - 1) / kSplitBM) * ((N + kSplitBN - 1) / kSplitBN) > 0x7FFFFFFF)
+    return BI_ERR_SHAPE;
+  return BI_OK;
+}
+
+// The partial kernel over (tiles, split_k), then the fixed-order fold; wsf
+// holds split_k * M * N floats.
+int splitk_launch(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t N,
+                  int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, int split_k, float *wsf,
+                  void *stream) {
   const int64_t tiles_m = (M + kSplitBM - 1) / kSplitBM, tiles_n = (N + kSplitBN - 1) / kSplitBN;
-  if (tiles_m * tiles_n > 0x7FFFFFFF) return BI_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
-  float *wsf = static_cast<float *>(ws);
   const int kc = (int)(K / split_k);
   if (kc % BK2 == 0)
     hipLaunchKernelGGL((gemm_partial_kernel<kSplitBN, kSplitBM, true>),
@@ -857,11 +894,30 @@ extern "C" int bi_gemm_splitk(const uint16_t *x, const uint16_t *w, uint16_t *y,
     hipLaunchKernelGGL((gemm_partial_kernel<kSplitBN, kSplitBM, false>),
                        dim3((unsigned)(tiles_m * tiles_n), (unsigned)split_k), dim3(kThreads), 0, s,
                        x, w, wsf, (int)M, (int)N, kc, ldx, ldw, (int)tiles_m, (int)tiles_n);
-  if ((st = launch_status()) != BI_OK) return st;
+  int st = launch_status();
+  if (st != BI_OK) return st;
   const int64_t groups = (M * N / 4 + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(gemm_splitk_combine_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, wsf,
                      y, (int)M, (int)N, split_k, ldy);
   return launch_status();
+}
+
+}  // namespace
+}  // namespace bi
+
+extern "C" int bi_gemm_splitk(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M,
+                              int64_t N, int64_t K, int64_t ldx, int64_t ldw, int64_t ldy,
+                              int split_k, void *ws, size_t ws_bytes, void *stream) {
+  const int st = splitk_validate(x, w, y, M, N, K, ldx, ldw, ldy, split_k);
+  if (st != BI_OK || M == 0) return st;
+  if (!ws) return BI_ERR_NULL;
+  if (ws_bytes < bi_gemm_splitk_workspace_bytes(M, N, split_k)) return BI_ERR_WORKSPACE;
+  if (!aligned16(ws)) return BI_ERR_ALIGN;
+  const Span sw{(uintptr_t)ws, (uintptr_t)ws + (uintptr_t)(split_k * M * N * 4)};
+  if (overlap(sw, span_of(y, M, N, ldy, 2)) || overlap(sw, span_of(x, M, K, ldx, 2)) ||
+      overlap(sw, span_of(w, N, K, ldw, 2)))
+    return BI_ERR_ALIAS;
+  return splitk_launch(x, w, y, M, N, K, ldx, ldw, ldy, split_k, static_cast<float *>(ws), stream);
 }
 
 extern "C" int bi_gemm_mswitch_control(const uint16_t *x, const uint16_t *w, uint16_t *y,

@@ -232,3 +232,77 @@ def test_gemm_fill_same_bits_as_bi_gemm(bi):
                                                       perm, "cuda")
         r = harness.batch_invariance(lambda xb: bi.bi_gemm_fill(xb, Wt), X, probes, batches)
         assert r["rows"] > 20 and r["diff_bits"] == 0, r
+
+
+def test_gemm_runs_one_config_at_every_m(bi):
+    """bi_gemm's output equals that of its own configuration
+    (bi_gemm_config_id(N, K), reported by bi_gemm_launch_plan) at every M: the
+    dynamic half of the static check that M selects nothing but the number of
+    workgroups."""
+    for N, K in ((4096, 4096), (1024, 4096)):
+        x = synth.normal_bf16((1000, K), 301 + N)
+        w = synth.normal_bf16((N, K), 302 + N, std=0.02)
+        X, Wt = dev_bf16(x), dev_bf16(w)
+        cfg = bi.bi_gemm_config_id(N, K)
+        kernels = {bi.bi_gemm_launch_plan(M, N, K)["kernel"] for M in (1, 33, 257, 1000)}
+        assert len(kernels) == 1
+        for M in (1, 33, 257, 1000):
+            say(f"gemm planned config N={N} K={K} M={M} cfg={cfg}")
+            assert torch.equal(bi.bi_gemm(X[:M], Wt).view(torch.int16),
+                               bi.bi_gemm_with_config(cfg, X[:M], Wt).view(torch.int16)), (N, K, M)
+
+
+def _two_term_sums(M: int, N: int, K: int, seed: int):
+    """x rows with two ones (columns 0 and 1 + m) and w rows chosen so that
+    every output y[m][n] = w[n][0] + w[n][1 + m] is a sum of two bf16 values
+    1..15 binades apart, exact in fp32 (at most 24 significant bits), that
+    then has to be rounded to bf16.  Mixed signs (cancellation), random
+    significands (odd and even neighbours), exact ties (the second term half an
+    output ulp), sums that carry into the next binade, and magnitudes from
+    2^-100 to 2^125 (no fp32 subnormals)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = np.zeros((M, K), np.uint16)
+    x[:, 0] = 0x3F80
+    x[np.arange(M), 1 + np.arange(M)] = 0x3F80
+    w = np.zeros((N, K), np.uint16)
+
+    def bits(sign, e, mant):
+        return ((sign.astype(np.uint32) << 15) | ((e + 127).astype(np.uint32) << 7)
+                | mant.astype(np.uint32)).astype(np.uint16)
+
+    E = g.integers(-100, 126, size=N)
+    sa = g.integers(0, 2, size=N)
+    ma = g.integers(0, 128, size=N)
+    ma[: N // 8] = 127                         # 1.1111111: rounding up carries
+    w[:, 0] = bits(sa, E, ma)
+    d = g.integers(1, 16, size=(N, M))
+    sb = g.integers(0, 2, size=(N, M))
+    mb = g.integers(0, 128, size=(N, M))
+    tie = g.random((N, M)) < 0.2                # b = +-2^(E-8): half an ulp of a
+    d[tie], mb[tie] = 8, 0
+    same = g.random((N, M)) < 0.5
+    sb[same] = np.repeat(sa[:, None], M, axis=1)[same]
+    w[:, 1:1 + M] = bits(sb, E[:, None] - d, mb)
+    return x, w
+
+
+def test_gemm_epilogue_rounds_arbitrary_fp32_sums(bi):
+    """The fp32 -> bf16 rounding of the epilogue against the oracle's
+    round-to-nearest-even, bit for bit, on 262,144 fp32 values that are not
+    integers: every output is an exact two-term sum (see _two_term_sums), so
+    its fp32 accumulator is exactly the fp64 oracle's value and only the final
+    rounding can differ."""
+    M, N, K = 64, 4096, 128
+    x, w = _two_term_sums(M, N, K, 4242)
+    exact = oracle.gemm(x, w)
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)  # exact in fp32
+    f32bits = exact.astype(np.float32).view(np.uint32)
+    ties = ((f32bits & 0xFFFF) == 0x8000).sum()
+    assert ties > 10000 and (exact != 0).all()
+    want = oracle.bf16_round(exact)
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    for cfg in range(bi.bi_gemm_num_configs()):
+        say(f"gemm rounding of two-term sums cfg={cfg}")
+        y = host_u16(bi.bi_gemm_with_config(cfg, X, Wt))
+        bad = y != want
+        assert not bad.any(), (cfg, int(bad.sum()), [hex(v) for v in f32bits[bad][:4]])
