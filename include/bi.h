@@ -19,8 +19,10 @@
  *     Weights are stored K-contiguous: the GEMM weight W as [N, K] (one output
  *     column per row) and the LoRA down-projection A as [R, K].
  *   - Pointers to tensors are DEVICE pointers (hipMalloc / torch), owned by the
- *     caller.  The library never allocates, frees or synchronises, and keeps no
- *     mutable global state; calls are thread-safe.
+ *     caller.  The library never allocates, frees or synchronises.  Its only
+ *     mutable global state belongs to bi_gemm_splitk_noalloc (a static device
+ *     scratch array per GPU and a lock-guarded cache of its address); every
+ *     other call is thread-safe without restriction.
  *   - stream is a hipStream_t passed as void*; NULL means the default stream.
  *     Every call is asynchronous on that stream.
  *   - Return value: a bi_status.  Arguments are validated before anything is
@@ -218,6 +220,34 @@ int bi_gemm_splitk(const uint16_t *x, const uint16_t *w, uint16_t *y,
 
 /* bi_gemm_splitk_workspace_bytes -- split_k * M * N * 4, rounded up to 256. */
 size_t bi_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int split_k);
+
+/* Size of the static scratch array behind bi_gemm_splitk_noalloc: 16 MiB per
+ * GPU, enough for M <= 64 at every Llama-3-8B and -70B projection with its
+ * bi_gemm_splitk_for split. */
+#define BI_GEMM_SPLITK_SCRATCH_BYTES (16u << 20)
+
+/*
+ * bi_gemm_splitk_noalloc -- bi_gemm_splitk for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * device allocation): the same kernels, the same bits, but the fp32 partials
+ * go to a static device array of BI_GEMM_SPLITK_SCRATCH_BYTES bytes inside the
+ * library instead of a caller's workspace.  The caller still passes x, w and
+ * y; the call allocates and frees nothing.
+ *
+ *   Arguments, layout and errors as bi_gemm_splitk without ws / ws_bytes.
+ *   BI_ERR_WORKSPACE when bi_gemm_splitk_workspace_bytes(M, N, split_k) >
+ *   BI_GEMM_SPLITK_SCRATCH_BYTES (nothing is launched).
+ *   The scratch belongs to the GPU of `stream` (the current device for NULL);
+ *   its address is looked up once per GPU, on the first call there.  Every
+ *   call on one GPU shares that GPU's array and nothing in it needs to start
+ *   at zero (each call writes every partial it folds), but calls that overlap
+ *   in time on one GPU -- concurrent streams, or host threads -- race on it
+ *   and must be serialised by the caller.  Unlike bi_gemm_splitk, the
+ *   partials are not returned.
+ */
+int bi_gemm_splitk_noalloc(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                           int64_t M, int64_t N, int64_t K,
+                           int64_t ldx, int64_t ldw, int64_t ldy, int split_k, void *stream);
 
 /* bi_gemm_splitk_for -- a split factor for (N, K) that fills the chip at M <= 64
  * (a power of two, at least 4 K-stages per chunk), or -1 if (N, K) is not

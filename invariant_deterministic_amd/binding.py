@@ -49,6 +49,8 @@ _lib_gemm_with_config = _sig("bi_gemm_with_config",
                              [_int, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p])
 _lib_gemm_splitk = _sig("bi_gemm_splitk", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _int, _p,
                                            ctypes.c_size_t, _p])
+_lib_gemm_splitk_noalloc = _sig("bi_gemm_splitk_noalloc", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64,
+                                                           _i64, _int, _p])
 _lib_gemm_splitk_ws = _sig("bi_gemm_splitk_workspace_bytes", [_i64, _i64, _int], ctypes.c_size_t)
 _lib_gemm_splitk_for = _sig("bi_gemm_splitk_for", [_i64, _i64])
 _lib_gemm_mswitch = _sig("bi_gemm_mswitch_control", [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -75,7 +77,7 @@ BI_OK = 0
 EXPORTS = ("bi_abi_version", "bi_status_str", "bi_rmsnorm", "bi_gemm", "bi_gemm_config_id",
            "bi_gemm_num_configs", "bi_gemm_with_config", "bi_gemm_launch_plan", "bi_gemm_fill", "bi_gemm_fill_config_id",
            "bi_gemm_splitk",
-           "bi_gemm_splitk_workspace_bytes", "bi_gemm_splitk_for", "bi_gemm_mswitch_control", "bi_lora_shrink_workspace_bytes",
+           "bi_gemm_splitk_workspace_bytes", "bi_gemm_splitk_for", "bi_gemm_splitk_noalloc", "bi_gemm_mswitch_control", "bi_lora_shrink_workspace_bytes",
            "bi_lora_shrink", "bi_lora_shrink_two_pass", "bi_lora_shrink_atomic", "bi_row_bitdiff",
            "bi_decode_attention", "bi_decode_attention_workspace_bytes", "bi_lora_expand",
            "bi_lora_shrink_expand")
@@ -270,6 +272,25 @@ def bi_gemm_splitk(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = No
     if split_k is None:
         split_k = bi_gemm_splitk_for(w.shape[0], w.shape[1])
     return _gemm_ws_call(_lib_gemm_splitk, "bi_gemm_splitk", x, w, y, split_k, ws, stream)
+
+
+GEMM_SPLITK_SCRATCH_BYTES = 16 << 20   # BI_GEMM_SPLITK_SCRATCH_BYTES
+
+
+def bi_gemm_splitk_noalloc(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,
+                           split_k: int | None = None, stream=None) -> torch.Tensor:
+    """bi_gemm_splitk with the partials in the library's static scratch: the
+    call allocates nothing (see bi.h).  Pass ``y`` to keep the wrapper itself
+    allocation-free too."""
+    M, N, K, y = _gemm_shapes(x, w, y)
+    if split_k is None:
+        split_k = bi_gemm_splitk_for(N, K)
+    px, ldx = _mat(x, "x", _BF16_LIKE)
+    pw, ldw = _mat(w, "w", _BF16_LIKE)
+    py, ldy = _mat(y, "y", _BF16_LIKE)
+    _check(_lib_gemm_splitk_noalloc(px, pw, py, M, N, K, ldx, ldw, ldy, split_k, _stream(stream)),
+           "bi_gemm_splitk_noalloc")
+    return y
 
 
 def bi_gemm_mswitch_control(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor | None = None,

@@ -30,6 +30,8 @@
 // stored, so no row's arithmetic depends on how many rows the batch holds.
 #include "common.h"
 
+#include <mutex>
+
 namespace bi {
 namespace {
 
@@ -902,6 +904,40 @@ int splitk_launch(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, 
   return launch_status();
 }
 
+// Scratch of the allocation-free split-K entry point: a static device array
+// (each GPU the library runs on holds its own copy until the process ends).
+// In host code its name is only a stand-in; the device address comes from
+// hipGetSymbolAddress, looked up once per device and kept here.
+static __device__ __align__(256) unsigned char scratch[BI_GEMM_SPLITK_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device of `stream` (the current device
+// for the null stream).
+int scratch_ptr(void *stream, void **out) {
+  int dev = 0;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return BI_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return BI_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return BI_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return BI_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return BI_ERR_HIP;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return BI_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return BI_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BI_OK;
+}
+
 }  // namespace
 }  // namespace bi
 
@@ -918,6 +954,21 @@ extern "C" int bi_gemm_splitk(const uint16_t *x, const uint16_t *w, uint16_t *y,
       overlap(sw, span_of(w, N, K, ldw, 2)))
     return BI_ERR_ALIAS;
   return splitk_launch(x, w, y, M, N, K, ldx, ldw, ldy, split_k, static_cast<float *>(ws), stream);
+}
+
+extern "C" int bi_gemm_splitk_noalloc(const uint16_t *x, const uint16_t *w, uint16_t *y,
+                                      int64_t M, int64_t N, int64_t K, int64_t ldx, int64_t ldw,
+                                      int64_t ldy, int split_k, void *stream) {
+  const int st = splitk_validate(x, w, y, M, N, K, ldx, ldw, ldy, split_k);
+  if (st != BI_OK || M == 0) return st;
+  if (bi_gemm_splitk_workspace_bytes(M, N, split_k) > (size_t)BI_GEMM_SPLITK_SCRATCH_BYTES)
+    return BI_ERR_WORKSPACE;
+  void *p = nullptr;
+  const int sp = scratch_ptr(stream, &p);
+  if (sp != BI_OK) return sp;
+  // every partial the fold reads is written first by the same call: nothing
+  // in the scratch has to start at zero
+  return splitk_launch(x, w, y, M, N, K, ldx, ldw, ldy, split_k, static_cast<float *>(p), stream);
 }
 
 extern "C" int bi_gemm_mswitch_control(const uint16_t *x, const uint16_t *w, uint16_t *y,

@@ -36,7 +36,7 @@ class _Guarded:
     # position of the batch-size argument in each launching entry point
     M_ARG = {"bi_rmsnorm": 3, "bi_gemm": 3, "bi_gemm_with_config": 4, "bi_gemm_fill": 3,
              "bi_lora_shrink": 3,
-             "bi_gemm_splitk": 3, "bi_gemm_mswitch_control": 3, "bi_decode_attention": 5, "bi_lora_expand": 4, "bi_lora_shrink_expand": 6,
+             "bi_gemm_splitk": 3, "bi_gemm_splitk_noalloc": 3, "bi_gemm_mswitch_control": 3, "bi_decode_attention": 5, "bi_lora_expand": 4, "bi_lora_shrink_expand": 6,
              "bi_lora_shrink_two_pass": 3, "bi_lora_shrink_atomic": 3, "bi_row_bitdiff": 6}
 
     def __init__(self, lib):
@@ -93,6 +93,7 @@ def _load():
     L.bi_gemm_splitk_workspace_bytes.argtypes = [i64, i64, i]
     L.bi_gemm_splitk_workspace_bytes.restype = ctypes.c_size_t
     L.bi_gemm_splitk_for.argtypes = [i64, i64]
+    L.bi_gemm_splitk_noalloc.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i, p]
     L.bi_gemm_mswitch_control.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, p, ctypes.c_size_t, p]
     L.bi_lora_shrink.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i, p, ctypes.c_size_t, p]
     L.bi_lora_shrink_two_pass.argtypes = L.bi_lora_shrink.argtypes
@@ -264,6 +265,15 @@ def test_gemm_splitk_validation(lib):
         s = lib.bi_gemm_splitk_for(N, K)
         assert s >= 1 and (s & (s - 1)) == 0 and K % (32 * s) == 0
     assert lib.bi_gemm_splitk_for(4096, 4096) == 8 and lib.bi_gemm_splitk_for(1024, 4096) == 32
+    h = lib.bi_gemm_splitk_noalloc
+    assert h(X, None, Y, *a, 8, None) == BI_ERR_NULL
+    assert h(X, W, Y, *a, 0, None) == BI_ERR_UNSUPPORTED
+    assert h(X, W, Y, 4, 4096, 4064, 4064, 4064, 4096, 8, None) == BI_ERR_SHAPE
+    assert h(X, W, X, *a, 8, None) == BI_ERR_ALIAS
+    # 8 * 128 * 4096 * 4 = 16 MiB fits the static scratch; one more row does not
+    assert lib.bi_gemm_splitk_workspace_bytes(129, 4096, 8) > 16 << 20
+    assert h(X, W, Y, 129, 4096, 4096, 4096, 4096, 4096, 8, None) == BI_ERR_WORKSPACE
+    assert h(None, W, None, 0, 4096, 4096, 4096, 4096, 4096, 8, None) == BI_OK
     g = lib.bi_gemm_mswitch_control
     assert g(X, W, Y, *a, None, need, None) == BI_ERR_NULL              # small M needs ws
     assert g(X, W, Y, 0, 4096, 4096, 4096, 4096, 4096, None, 0, None) == BI_OK
