@@ -14,7 +14,8 @@
 // over the same k steps; configurations differ only in how many outputs one
 // workgroup owns.  The configuration is picked from (N, K) alone.
 //
-// Data path per workgroup (4 wavefronts, 2 x 2 over the tile):
+// Data path per workgroup (4 wavefronts, 2 x 2 over the tile; the 256 x 256
+// tile's 64-k kernel runs 8 wavefronts in two ping-pong groups instead):
 //   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS
 //          --ds_read_b128--> VGPR fragments --MFMA--> fp32 accumulators
 //   epilogue: accumulators -> bf16 (round to nearest even) -> LDS -> whole
@@ -671,19 +672,177 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_combine_kernel(
   *reinterpret_cast<u32x2 *>(y + m * ldy + n) = o;
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong variant of the 64-k kernel: 8 wavefronts, two per SIMD (wave w
+// runs on SIMD w & 3), in two groups g = w >> 2.  SIMD q owns quadrant
+// (q >> 1, q & 1) of the tile, QN x QM; wave (q, g) owns half g of it along m,
+// QN x QM/2.  A stage is one phase of fragment reads and one phase of
+// matrix-core steps per wave; the groups run these phases in opposition --
+// while group 0 reads stage j's fragments, group 1 multiplies stage j - 1, and
+// the other way round -- separated by workgroup barriers (group 1 starts one
+// barrier late and group 0 ends one barrier later), so each SIMD's matrix core
+// always has one wave's products to run while the other wave waits on LDS.
+// Group 0 loads the weights (a ring of 2 stages, the next stage issued one
+// stage ahead), group 1 the activations (a ring of 3, two stages ahead).
+// Every accumulator still receives its 16-k steps in ascending order from one
+// wave, so the bits equal the 4-wave kernels'.
+//
+// Stage timing (B(i): the i-th barrier; phases between them):
+//   group 0 reads stage j in (B(2j), B(2j+1)), multiplies it in (B(2j+1), B(2j+2));
+//   group 1 reads stage j in (B(2j+1), B(2j+2)), multiplies it in (B(2j+2), B(2j+3)).
+//   Stage j's slots are free after B(2j+2).  Group 0 issues weight stage j+1
+//   while reading stage j (slot of j-1) and waits for it before B(2j+2);
+//   group 1 issues activation stage j+2 while reading stage j (slot of j-1)
+//   and waits for stage j+1 before B(2j+2).
+template <int FN, int FM>
+__device__ __forceinline__ void store_sub(const f32x16 (&acc)[FN][FM], char *mine, uint16_t *y,
+                                          int M, int N, int64_t ldy, int m_org, int n_org,
+                                          int lane) {
+  constexpr int WN = FN * 32, WM = FM * 32;
+  constexpr int CH = WN / 8, ROWB = WN * 2, HB = CH / 2;
+  static_assert(CH == 8 || CH == 16, "sub-tile width");
+  auto f = [](int m) { return ((m & 1) * HB) | ((m >> 1) & (HB - 1)); };
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int m = j * 32 + (lane & 31);
+    char *row = mine + m * ROWB + (lane >> 5) * 8;
+    const int fm = f(m);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint2 o;
+        o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+        o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+        *reinterpret_cast<uint2 *>(row + (((i * 4 + q) ^ fm) << 4)) = o;
+      }
+    }
+  }
+  constexpr int SEG = CH / 8;
+#pragma unroll 4
+  for (int t = 0; t < WM / 8 * SEG; ++t) {
+    const int r = (t / SEG) * 8 + (lane >> 3);
+    const int c = (t % SEG) * 8 + (lane & 7);
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(mine + r * ROWB + ((c ^ f(r)) << 4));
+    const int m = m_org + r, n = n_org + c * 8;
+    if (m < M && n < N) *reinterpret_cast<u32x4 *>(y + (int64_t)m * ldy + n) = v;
+  }
+}
+
+template <int BN, int BM>
+__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+  constexpr int QN = BN / 2, QM = BM / 2, WM = QM / 2;
+  constexpr int FN = QN / 32, FM = WM / 32;
+  constexpr int WB = BN * kRow2, XB = BM * kRow2;
+  constexpr int LW = BN / 32, LX = BM / 32;
+  static_assert(2 * WB + 3 * XB <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * WB + 3 * XB];
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = wave & 3, g = wave >> 2;
+  const int nw = (q >> 1) * QN, mw = (q & 1) * QM + g * WM;
+  const int nkb = K / BK2;
+  char *const ws0 = lds, *const ws1 = lds + WB;
+  char *const xs0 = lds + 2 * WB, *const xs1 = xs0 + XB, *const xs2 = xs1 + XB;
+  static_assert(BN == BM, "one load plan per group");
+  LoadPlan2<BN> pl;  // group 0: rows of w; group 1: rows of x
+  if (g == 0) pl.init(w, N, n0, N, ldw, K, q, lane);
+  else pl.init(x, M, m0, M, ldx, K, q, lane);
+  LoadPlan2<BN> &pw = pl, &px = pl;
+  f32x16 acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = f32x16{};
+
+  if (g == 0) {
+    pw.issue(ws0, 0, q);
+    if (nkb > 1) {
+      pw.issue(ws1, BK2, q);
+      wait_vmcnt<LW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  } else {
+    px.issue(xs0, 0, q);
+    if (nkb > 1) px.issue(xs1, BK2, q);
+    if (nkb > 2) px.issue(xs2, 2 * BK2, q);
+    if (nkb > 2) wait_vmcnt<2 * LX>();
+    else if (nkb > 1) wait_vmcnt<LX>();
+    else wait_vmcnt<0>();
+  }
+  barrier_no_fence();
+  if (g == 1) barrier_no_fence();
+
+  bf16x8 fa[4][FN], fb[4][FM];
+  for (int j = 0; j < nkb; ++j) {
+    const char *wc = (j & 1) ? ws1 : ws0;
+    const int js = j % 3;
+    const char *xc = js == 0 ? xs0 : (js == 1 ? xs1 : xs2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i) fa[ks][i] = read_frag2(wc, nw + i * 32 + (lane & 31), ks, lane);
+#pragma unroll
+      for (int jj = 0; jj < FM; ++jj) fb[ks][jj] = read_frag2(xc, mw + jj * 32 + (lane & 31), ks, lane);
+    }
+    if (g == 0) {
+      if (j >= 1 && j + 1 < nkb) pw.issue((j & 1) ? ws0 : ws1, (j + 1) * BK2, q);
+    } else {
+      if (j >= 1 && j + 2 < nkb) {
+        const int ns = (j + 2) % 3;
+        px.issue(ns == 0 ? xs0 : (ns == 1 ? xs1 : xs2), (j + 2) * BK2, q);
+      }
+    }
+    wait_lgkmcnt0();
+    if (g == 1) {
+      if (j + 2 < nkb) wait_vmcnt<LX>();
+      else wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    barrier_no_fence();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FM; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][jj], acc[i][jj], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (g == 0) wait_vmcnt<0>();
+    barrier_no_fence();
+  }
+  if (g == 0) barrier_no_fence();
+  // every stage read is done and no load is in flight: the LDS is free for the
+  // epilogue, one QN x WM region per wave
+  store_sub<FN, FM>(acc, lds + wave * (WM * QN * 2), y, M, N, ldy, m0 + mw, n0 + nw, lane);
+}
+
 typedef void (*GemmKernel)(const uint16_t *, const uint16_t *, uint16_t *, int, int, int, int64_t,
                            int64_t, int64_t, int, int);
 struct CfgEntry {
   int bn, bm;
-  GemmKernel kernel;  // BK = 32 stages, any K % 32 == 0
+  GemmKernel kernel;  // BK = 32 stages, any K % 32 == 0 (256 threads)
   GemmKernel wide;    // BK = 64 stages, used when K % 64 == 0 (same k order, same bits)
+  int wide_threads;   // workgroup size of `wide`
 };
 
+// The 256 x 256 tile's 64-k kernel is the 8-wavefront ping-pong one.  Under
+// full load the card runs at its power limit and the 4-wavefront kernel does
+// as well; with fewer tiles than compute units (for example M = 2048 at
+// N = 4096) the ping-pong kernel's busier matrix cores pay off.
 const CfgEntry kConfigs[] = {
-    {256, 256, gemm_kernel<256, 256>, gemm_wide_kernel<256, 256>},
-    {256, 128, gemm_kernel<256, 128>, gemm_wide_kernel<256, 128>},
-    {128, 128, gemm_kernel<128, 128>, gemm_wide_kernel<128, 128>},
-    {128, 256, gemm_kernel<128, 256>, gemm_wide_kernel<128, 256>},
+    {256, 256, gemm_kernel<256, 256>, gemm_pp_kernel<256, 256>, 512},
+    {256, 128, gemm_kernel<256, 128>, gemm_wide_kernel<256, 128>, kThreads},
+    {128, 128, gemm_kernel<128, 128>, gemm_wide_kernel<128, 128>, kThreads},
+    {128, 256, gemm_kernel<128, 256>, gemm_wide_kernel<128, 256>, kThreads},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -762,22 +921,22 @@ int validate(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64
 // number of tile rows (how many workgroups run), never the kernel, its tile or
 // its K stage.
 struct Plan {
-  int cfg, bm, bn, kstage;
+  int cfg, bm, bn, kstage, threads;
   int64_t tiles_m, tiles_n;
   GemmKernel kern;
 };
 Plan plan_for(int cfg, int64_t M, int64_t N, int64_t K) {
   const CfgEntry &c = kConfigs[cfg];
   const bool wide = c.wide && K % BK2 == 0;
-  return Plan{cfg, c.bm, c.bn, wide ? BK2 : BK, (M + c.bm - 1) / c.bm, (N + c.bn - 1) / c.bn,
-              wide ? c.wide : c.kernel};
+  return Plan{cfg, c.bm, c.bn, wide ? BK2 : BK, wide ? c.wide_threads : kThreads,
+              (M + c.bm - 1) / c.bm, (N + c.bn - 1) / c.bn, wide ? c.wide : c.kernel};
 }
 
 int launch(int cfg, const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t N,
            int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, void *stream) {
   const Plan p = plan_for(cfg, M, N, K);
   if (p.tiles_m * p.tiles_n > 0x7FFFFFFF) return BI_ERR_SHAPE;
-  hipLaunchKernelGGL(p.kern, dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(kThreads), 0,
+  hipLaunchKernelGGL(p.kern, dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(p.threads), 0,
                      (hipStream_t)stream, x, w, y, (int)M, (int)N, (int)K, ldx, ldw, ldy,
                      (int)p.tiles_m, (int)p.tiles_n);
   return launch_status();
@@ -816,7 +975,7 @@ extern "C" int bi_gemm_launch_plan(int64_t M, int64_t N, int64_t K, int64_t *pla
   plan[2] = p.bm;
   plan[3] = p.bn;
   plan[4] = p.kstage;
-  plan[5] = kThreads;
+  plan[5] = p.threads;
   plan[6] = M == 0 ? 0 : p.tiles_m * p.tiles_n;
   return BI_OK;
 }
