@@ -314,6 +314,24 @@ def metric_parts(bi, torch, dev, H, Wq, Wkv, Wup, Wdown, A, G, eps):
           file=sys.stderr, flush=True)
     res["rmsnorm"] = r_out
 
+    # The practical ceiling beside the 8 TB/s spec: a plain device copy (torch)
+    # of the bytes RMSNorm moves at M = 2048 and 8192 (16 and 64 MiB each
+    # way), rotated the same way
+    ref = {}
+    for mib in (16, 64):
+        nb = mib << 20
+        c = _copies(2 * nb)
+        srcs = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(c)]
+        dsts = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(c)]
+        ms = _time_loop(torch, lambda i: dsts[i % c].copy_(srcs[i % c]), 4 * c)
+        gbs = 2.0 * nb / (ms * 1e-3) / 1e9
+        ref[f"{mib}MiB_each_way"] = {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                                     "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        del srcs, dsts
+    r_out["device_copy_reference"] = ref
+    print(f"# device copy: " + ", ".join(f"{k} {v['frac']:.3f}" for k, v in ref.items()),
+          file=sys.stderr, flush=True)
+
     # LoRA shrink at M = 4096, x rotated over >= 1 GiB
     M, K, R = 4096, 4096, R_LORA
     c = _copies(2 * M * K)
@@ -570,11 +588,15 @@ def cpu_baseline(x, g, ws_h, a, eps):
                       "and again to feed Down)"}
 
 
-def _time_loop(torch, fn, n, reps=7):
+def _time_loop(torch, fn, n, reps=7, warm_s=0.03):
     """Median over reps of (n launches) / n, in ms.  The n launches are
     captured once in a HIP graph and the graph is replayed between HIP events,
     so the figure is device time, not the host's launch rate (the kernels here
-    issue no memset, which keeps them safe to capture)."""
+    issue no memset, which keeps them safe to capture).  Untimed replays fill
+    the first ``warm_s`` seconds: the card's clock follows its load with a
+    delay of milliseconds, so a point timed right after a different load
+    (full-chip GEMMs before a half-chip one, say) would otherwise measure the
+    previous load's clock."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -588,6 +610,10 @@ def _time_loop(torch, fn, n, reps=7):
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + warm_s
+    while time.perf_counter() < t_end:
+        g.replay()
+        torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
         e0 = torch.cuda.Event(enable_timing=True)
