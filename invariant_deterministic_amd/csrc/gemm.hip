@@ -682,18 +682,20 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_combine_kernel(
 // the other way round -- separated by workgroup barriers (group 1 starts one
 // barrier late and group 0 ends one barrier later), so each SIMD's matrix core
 // always has one wave's products to run while the other wave waits on LDS.
-// Group 0 loads the weights (a ring of 2 stages, the next stage issued one
-// stage ahead), group 1 the activations (a ring of 3, two stages ahead).
+// Group 0 loads the activations (a ring of 2 stages, the next stage issued
+// one stage ahead), group 1 the weights (a ring of 3, two stages ahead): with
+// few rows the weights are the stream that matters, and the ring of 3 gives
+// their loads three phases to land instead of two.
 // Every accumulator still receives its 16-k steps in ascending order from one
 // wave, so the bits equal the 4-wave kernels'.
 //
 // Stage timing (B(i): the i-th barrier; phases between them):
 //   group 0 reads stage j in (B(2j), B(2j+1)), multiplies it in (B(2j+1), B(2j+2));
 //   group 1 reads stage j in (B(2j+1), B(2j+2)), multiplies it in (B(2j+2), B(2j+3)).
-//   Stage j's slots are free after B(2j+2).  Group 0 issues weight stage j+1
-//   while reading stage j (slot of j-1) and waits for it before B(2j+2);
-//   group 1 issues activation stage j+2 while reading stage j (slot of j-1)
-//   and waits for stage j+1 before B(2j+2).
+//   Stage j's slots are free after B(2j+2).  Group 0 issues activation stage
+//   j+1 while reading stage j (slot of j-1) and waits for it before B(2j+2);
+//   group 1 issues weight stage j+2 while reading stage j (slot of j-1) and
+//   waits for stage j+1 before B(2j+2).
 template <int FN, int FM>
 __device__ __forceinline__ void store_sub(const f32x16 (&acc)[FN][FM], char *mine, uint16_t *y,
                                           int M, int N, int64_t ldy, int m_org, int n_org,
@@ -737,8 +739,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   constexpr int FN = QN / 32, FM = WM / 32;
   constexpr int WB = BN * kRow2, XB = BM * kRow2;
   constexpr int LW = BN / 32, LX = BM / 32;
-  static_assert(2 * WB + 3 * XB <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) char lds[2 * WB + 3 * XB];
+  static_assert(2 * XB + 3 * WB <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * XB + 3 * WB];
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -747,13 +749,12 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   const int q = wave & 3, g = wave >> 2;
   const int nw = (q >> 1) * QN, mw = (q & 1) * QM + g * WM;
   const int nkb = K / BK2;
-  char *const ws0 = lds, *const ws1 = lds + WB;
-  char *const xs0 = lds + 2 * WB, *const xs1 = xs0 + XB, *const xs2 = xs1 + XB;
+  char *const xs0 = lds, *const xs1 = lds + XB;                          // ring of 2
+  char *const ws0 = lds + 2 * XB, *const ws1 = ws0 + WB, *const ws2 = ws1 + WB;  // ring of 3
   static_assert(BN == BM, "one load plan per group");
-  LoadPlan2<BN> pl;  // group 0: rows of w; group 1: rows of x
-  if (g == 0) pl.init(w, N, n0, N, ldw, K, q, lane);
-  else pl.init(x, M, m0, M, ldx, K, q, lane);
-  LoadPlan2<BN> &pw = pl, &px = pl;
+  LoadPlan2<BN> pl;  // group 0: rows of x; group 1: rows of w
+  if (g == 0) pl.init(x, M, m0, M, ldx, K, q, lane);
+  else pl.init(w, N, n0, N, ldw, K, q, lane);
   f32x16 acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
@@ -761,19 +762,19 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     for (int j = 0; j < FM; ++j) acc[i][j] = f32x16{};
 
   if (g == 0) {
-    pw.issue(ws0, 0, q);
+    pl.issue(xs0, 0, q);
     if (nkb > 1) {
-      pw.issue(ws1, BK2, q);
-      wait_vmcnt<LW>();
+      pl.issue(xs1, BK2, q);
+      wait_vmcnt<LX>();
     } else {
       wait_vmcnt<0>();
     }
   } else {
-    px.issue(xs0, 0, q);
-    if (nkb > 1) px.issue(xs1, BK2, q);
-    if (nkb > 2) px.issue(xs2, 2 * BK2, q);
-    if (nkb > 2) wait_vmcnt<2 * LX>();
-    else if (nkb > 1) wait_vmcnt<LX>();
+    pl.issue(ws0, 0, q);
+    if (nkb > 1) pl.issue(ws1, BK2, q);
+    if (nkb > 2) pl.issue(ws2, 2 * BK2, q);
+    if (nkb > 2) wait_vmcnt<2 * LW>();
+    else if (nkb > 1) wait_vmcnt<LW>();
     else wait_vmcnt<0>();
   }
   barrier_no_fence();
@@ -781,9 +782,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
 
   bf16x8 fa[4][FN], fb[4][FM];
   for (int j = 0; j < nkb; ++j) {
-    const char *wc = (j & 1) ? ws1 : ws0;
+    const char *xc = (j & 1) ? xs1 : xs0;
     const int js = j % 3;
-    const char *xc = js == 0 ? xs0 : (js == 1 ? xs1 : xs2);
+    const char *wc = js == 0 ? ws0 : (js == 1 ? ws1 : ws2);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -793,16 +794,16 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
       for (int jj = 0; jj < FM; ++jj) fb[ks][jj] = read_frag2(xc, mw + jj * 32 + (lane & 31), ks, lane);
     }
     if (g == 0) {
-      if (j >= 1 && j + 1 < nkb) pw.issue((j & 1) ? ws0 : ws1, (j + 1) * BK2, q);
+      if (j >= 1 && j + 1 < nkb) pl.issue((j & 1) ? xs0 : xs1, (j + 1) * BK2, q);
     } else {
       if (j >= 1 && j + 2 < nkb) {
         const int ns = (j + 2) % 3;
-        px.issue(ns == 0 ? xs0 : (ns == 1 ? xs1 : xs2), (j + 2) * BK2, q);
+        pl.issue(ns == 0 ? ws0 : (ns == 1 ? ws1 : ws2), (j + 2) * BK2, q);
       }
     }
     wait_lgkmcnt0();
     if (g == 1) {
-      if (j + 2 < nkb) wait_vmcnt<LX>();
+      if (j + 2 < nkb) wait_vmcnt<LW>();
       else wait_vmcnt<0>();
     }
     __builtin_amdgcn_sched_barrier(0);
