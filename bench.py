@@ -9,7 +9,8 @@ at Llama-3-8B projection shapes (K = 4096):
     D  = bi_gemm(U, Wdown)  K = 14336, N = 4096
     L  = bi_lora_shrink(H, A, split 8)   and the unsplit pass and the atomic
          control (A [16, 4096] ~ N(0, 0.01^2), fp32 out)
-    bi_row_bitdiff: probe rows of Q and D against the same rows computed alone
+    bi_row_bitdiff: probe rows of every output (H, Q, KV, U, D, L, Lu) against
+         the same rows computed alone, counted on every timed step
 Inputs are resident in HBM before timing starts.  ``value`` is the step's
 algorithmic TFLOP/s (2*M*N*K per GEMM, 2*M*R*K per shrink) over the timed
 steps.  ``roofline`` is for the dominant kernel (the 256x256-tile GEMM, which
@@ -19,9 +20,18 @@ of the same step.  ``clock`` is the shader clock and socket power read during
 the untimed settle steps, and the dominant kernel's fraction of the MFMA peak
 scaled to that clock (the published peak assumes 2.4 GHz).
 
+After the step, the rest of the headline metric is graph-timed on its own:
+``gemm_over_m`` (bi_gemm at M = 2048, 4096, 8192 on the four projections, with
+geometric means), ``rmsnorm`` (GB/s over rotated copies, beside a plain device
+copy of the same bytes), ``shrink`` (the variants at M = 4096 and the two
+latency ratios the LoRA page reports), the shrink's replay variation, and
+``stream70b`` (the Llama-3-70B MLP shape over a 200-batch dynamic stream).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--M 4096]
+       [--step-only]    skip the metric parts after the step
        [--sweep FILE]   also time each kernel over an M sweep (JSONL to FILE)
-       [--only NAME]    run only one kernel repeatedly (for rocprofv3 counters)
+       [--replays FILE] also run the 1000-replay shrink protocol at every M
+       [--only NAME]    run only one kernel repeatedly (for rocprofv3 runs)
 """
 from __future__ import annotations
 
