@@ -19,6 +19,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxChunks = 8;  // 16-byte chunks per thread: K <= 8 * 256 * 8
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 // NCH: 16-byte chunks a thread may own (1, 2, 4 or 8), picked from K alone so
 // that the registers fit the row and nothing about the reduction changes.
 // RPW: rows per workgroup, one after another through the same 256 threads;
@@ -54,11 +59,12 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
   }
 
   __shared__ float part[RPW][kThreads / 64];
+  float ss[RPW];
 #pragma unroll
   for (int q = 0; q < RPW; ++q) {
     // Thread-local sum of squares in ascending element order.  Each square of
     // a bf16 value is exact in fp32, so only the additions round.
-    float ss = 0.0f;
+    ss[q] = 0.0f;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = t + i * kThreads;
@@ -67,18 +73,42 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
         for (int j = 0; j < 4; ++j) {
           const float a = lo_bf16(v[q][i][j]);
           const float b = hi_bf16(v[q][i][j]);
-          ss = ss + a * a;
-          ss = ss + b * b;
+          ss[q] = ss[q] + a * a;
+          ss[q] = ss[q] + b * b;
         }
       }
     }
-    // Wavefront: fixed xor butterfly.  Partners add the same two values (in
-    // swapped operand order, which is exact-commutative), so every lane ends
-    // with the same bits.
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss = ss + __shfl_xor(ss, off, 64);
-    if ((t & 63) == 0) part[q][t >> 6] = ss;
   }
+  // Wavefront: fixed xor butterfly over lane offsets 32, 16, 8, 4, 2, 1, each
+  // step own + partner.  Partners add the same two values (in swapped operand
+  // order, which is exact-commutative), so after the step of offset d the
+  // lanes i and i ^ d hold the same bits.  The two steps that cross 16-lane
+  // rows use the LDS permute; the four inside a row are DPP lane moves in the
+  // VALU: offset 8 is a rotation of the row by 8 (lane i takes (i - 8) mod 16
+  // = i ^ 8); offset 4 a rotation by 4, since (i - 4) mod 16 is i ^ 4 or
+  // (i ^ 4) ^ 8, which hold the same value by then; offsets 2 and 1 exact
+  // quad permutations.  The rows of a workgroup go through each step
+  // together.
+  auto dpp_add = [](float x, auto ctrl) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                            0, __builtin_bit_cast(int, x), decltype(ctrl)::value,
+                                            0xF, 0xF, false));
+  };
+#pragma unroll
+  for (int off = 32; off >= 16; off >>= 1)
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) ss[q] = ss[q] + __shfl_xor(ss[q], off, 64);
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) ss[q] = dpp_add(ss[q], IntC<0x128>{});  // row_ror:8
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) ss[q] = dpp_add(ss[q], IntC<0x124>{});  // row_ror:4
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) ss[q] = dpp_add(ss[q], IntC<0x4E>{});   // quad_perm [2,3,0,1]
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) ss[q] = dpp_add(ss[q], IntC<0xB1>{});   // quad_perm [1,0,3,2]
+#pragma unroll
+  for (int q = 0; q < RPW; ++q)
+    if ((t & 63) == 0) part[q][t >> 6] = ss[q];
   __syncthreads();
 
 #pragma unroll
