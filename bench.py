@@ -569,13 +569,13 @@ def recorded_traffic():
 
 
 def cpu_baseline(x, g, ws_h, a, eps):
-    """The oracle as it stands, on a bounded sample of one step: 64 rows through
-    RMSNorm, the four projections and the shrink (about 25 GFLOP of fp64,
+    """The oracle as it stands, on a bounded sample of one step: 80 rows through
+    RMSNorm, the four projections and the shrink (about 31 GFLOP of fp64,
     10-20 s on the host cores)."""
     import numpy as np
 
     import oracle
-    rows = 64
+    rows = 80
     xs = x[:rows]
     t = time.perf_counter()
     h = oracle.rmsnorm(xs, g, eps)
