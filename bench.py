@@ -549,10 +549,21 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_256x256_llama8b_m4096_hbm
 GEMM_SOURCE = os.path.join(ROOT, "invariant_deterministic_amd", "csrc", "gemm.hip")
 
 
+def code_sha256(path: str) -> str:
+    """sha256 of a C/HIP source with its comments and whitespace removed, so
+    that it changes with the code and not with the commentary."""
+    import hashlib
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
 def recorded_traffic():
     """HBM bytes per launch of the dominant GEMM from the committed rocprofv3
-    counter summary, or None when the kernel source changed since."""
-    import hashlib
+    counter summary, or None when the kernel code changed since the counters
+    were taken."""
     try:
         text = open(TRAFFIC_PROFILE).read()
     except OSError:
@@ -562,8 +573,7 @@ def recorded_traffic():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.split()[0] if v.split() else ""
-    cur = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-    if fields.get("source_sha256") != cur or "traffic_bytes_per_launch" not in fields:
+    if fields.get("code_sha256") != code_sha256(GEMM_SOURCE) or "traffic_bytes_per_launch" not in fields:
         return None
     return float(fields["traffic_bytes_per_launch"])
 

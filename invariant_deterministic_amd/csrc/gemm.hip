@@ -673,10 +673,11 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Ping-pong variant of the 64-k kernel: 8 wavefronts, two per SIMD (wave w
-// runs on SIMD w & 3), in two groups g = w >> 2.  SIMD q owns quadrant
-// (q >> 1, q & 1) of the tile, QN x QM; wave (q, g) owns half g of it along m,
-// QN x QM/2.  A stage is one phase of fragment reads and one phase of
+// Ping-pong variant of the 64-k kernel: 8 wavefronts, two per SIMD (the
+// dispatcher places wave w on SIMD w & 3; only the overlap described below,
+// never a result, depends on that placement), in two groups g = w >> 2.
+// SIMD q owns quadrant (q >> 1, q & 1) of the tile, QN x QM; wave (q, g) owns
+// half g of it along m, QN x QM/2.  A stage is one phase of fragment reads and one phase of
 // matrix-core steps per wave; the groups run these phases in opposition --
 // while group 0 reads stage j's fragments, group 1 multiplies stage j - 1, and
 // the other way round -- separated by workgroup barriers (group 1 starts one

@@ -2,7 +2,6 @@
 the clock summary and the multi-GPU refusal."""
 from __future__ import annotations
 
-import hashlib
 import os
 import subprocess
 import sys
@@ -14,19 +13,21 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 
-def test_recorded_traffic_tracks_the_gemm_source(tmp_path, monkeypatch):
+def test_recorded_traffic_tracks_the_gemm_code(tmp_path, monkeypatch):
     src = tmp_path / "gemm.hip"
-    src.write_bytes(b"kernel source v1\n")
-    sha = hashlib.sha256(src.read_bytes()).hexdigest()
+    src.write_text("// kernel v1\nint f() { return 1; }\n")
+    sha = bench.code_sha256(str(src))
     prof = tmp_path / "prof.txt"
     prof.write_text("# header: ignored\n"
-                    f"source_sha256: {sha}   (at collection time)\n"
+                    f"code_sha256: {sha}   (at collection time)\n"
                     "traffic_bytes_per_launch: 6.25e+08\n")
     monkeypatch.setattr(bench, "GEMM_SOURCE", str(src))
     monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(prof))
     assert bench.recorded_traffic() == 6.25e8
-    src.write_bytes(b"kernel source v2\n")           # the kernel changed since the counters
-    assert bench.recorded_traffic() is None
+    src.write_text("/* reworded */ // kernel v1, same code\nint f()  {\n  return 1; }\n")
+    assert bench.recorded_traffic() == 6.25e8      # commentary and layout only
+    src.write_text("// kernel v1\nint f() { return 2; }\n")
+    assert bench.recorded_traffic() is None         # the code changed since the counters
     monkeypatch.setattr(bench, "TRAFFIC_PROFILE", str(tmp_path / "missing.txt"))
     assert bench.recorded_traffic() is None
 
