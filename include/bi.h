@@ -100,8 +100,8 @@ int bi_rmsnorm(const uint16_t *x, const uint16_t *w, uint16_t *y,
  *   y   [M, N] bf16, row stride ldy (output; must not overlap x or w)
  *   M >= 0; N >= 8, N % 8 == 0; K >= 32, K % 32 == 0; x and w each span
  *   fewer than 2^31 elements ((rows - 1) * ld + K).
- * Reduction order of every output: one ascending pass over K in steps of 16
- * (one bf16 32x32x16 matrix-core instruction per step, fp32 accumulator
+ * Reduction order of every output: one ascending pass over K in steps of 32
+ * (one bf16 16x16x32 matrix-core instruction per step, fp32 accumulator
  * rounded between steps); no split-K, no stream-K.  The tile configuration is
  * bi_gemm_config_id(N, K): it never reads M.  Output rounding is
  * round-to-nearest-even.
@@ -137,7 +137,7 @@ int bi_gemm_config_id(int64_t N, int64_t K);
  *          [0] configuration (= bi_gemm_config_id(N, K)),
  *          [1] kernel id (which compiled kernel runs),
  *          [2] tile rows (of M), [3] tile columns (of N),
- *          [4] k per LDS stage (32 or 64; the 16-k matrix-core steps are the
+ *          [4] k per LDS stage (32 or 64; the 32-k matrix-core steps are the
  *              same either way), [5] threads per workgroup,
  *          [6] workgroups = ceil(M / tile rows) * ceil(N / tile columns)
  *              (0 when M == 0).
@@ -209,7 +209,7 @@ int bi_gemm_fill_config_id(int64_t M, int64_t N, int64_t K);
  *       bi_gemm_splitk_workspace_bytes(M, N, split_k) bytes; on return it holds
  *       the partial sums p_s[m][n] at ws[(s * M + m) * N + n].
  * Reduction order of every output: chunk s covers k in [s*K/S, (s+1)*K/S),
- * one ascending pass in 16-k steps (the bi_gemm main loop over that range);
+ * one ascending pass in 32-k steps (the bi_gemm main loop over that range);
  * then bf16( (((p_0 + p_1) + p_2) + ...) + p_{S-1} ) in fp32, rounded to nearest
  * even once.  split_k == 1 gives bi_gemm's bits.
  */

@@ -6,13 +6,18 @@
 // (no split-K chosen for small batches), accepting some lost speed.
 //
 // Reduction order of every output element (the batch-invariance contract):
-// one pass over k = 0, 16, 32, ..., K-16, each step a single
-// v_mfma_f32_32x32x16_bf16 whose fp32 accumulator is rounded between steps.
+// one pass over k = 0, 32, 64, ..., K-32, each step a single
+// v_mfma_f32_16x16x32_bf16 whose fp32 accumulator is rounded between steps.
 // The order never depends on M, on the tile the element falls in, on the
-// position of the element inside its 32x32 matrix-core block, or on the
+// position of the element inside its 16x16 matrix-core block, or on the
 // tile configuration: every configuration below runs the same instruction
 // over the same k steps; configurations differ only in how many outputs one
 // workgroup owns.  The configuration is picked from (N, K) alone.
+//
+// Why 16x16x32 and not 32x32x16 (same peak rate): at full load the card sits
+// at its socket power limit, and measured under sustained load the 16x16x32
+// form runs the same kernels at a ~10 % higher shader clock for the same
+// power, 5-9 % more throughput at M >= 4096.
 //
 // Data path per workgroup (4 wavefronts, 2 x 2 over the tile; the 256 x 256
 // tile's 64-k kernel runs 8 wavefronts in two ping-pong groups instead):
@@ -26,7 +31,8 @@
 //     request is a full line; one operand in a ring of 3 stages, the other in
 //     a ring of 2 (160 KiB of LDS at 256 x 256).
 // Each LDS row's 16-byte chunks are XOR-permuted by a function of the row so
-// that the 32 rows a fragment read touches spread over all LDS banks.  Rows
+// that the 16 rows a quarter-wavefront's fragment read touches spread over all
+// LDS banks.  Rows
 // beyond M (or N) are loaded as copies of the last valid row and never
 // stored, so no row's arithmetic depends on how many rows the batch holds.
 #include "common.h"
@@ -37,21 +43,20 @@ namespace bi {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BK = 32;                 // k per LDS stage (two 16-k matrix-core steps)
+constexpr int BK = 32;                 // k per LDS stage (one 32-k matrix-core step)
 constexpr int kRowBytes = BK * 2;      // one LDS row: 32 bf16 = four 16-byte chunks
 constexpr int kStages = 4;             // LDS ring depth: 3 stages of loads in flight
 
 // Chunk permutation of LDS row r (4 chunks of 16 bytes): chunk c of row r is
-// stored at c ^ ((r >> 2) & 3).  A fragment read (32 rows, one chunk each, per
-// half-wavefront) then hits each 16-byte bank group of every 256-byte LDS
-// window once per 16 lanes -- conflict-free; measured on gfx950 with four
-// wavefronts reading concurrently, where the plain layout costs 2x.
+// stored at c ^ ((r >> 2) & 3).  A fragment read (16 consecutive rows, one
+// chunk each, per quarter-wavefront) then hits each 16-byte bank group of the
+// four 256-byte LDS windows those rows span once -- conflict-free.
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 template <int BN, int BM>
 struct Cfg {
   static constexpr int WN = BN / 2, WM = BM / 2;    // wavefront tile (n x m)
-  static constexpr int FN = WN / 32, FM = WM / 32;  // 32x32 blocks per wavefront
+  static constexpr int FN = WN / 16, FM = WM / 16;  // 16x16 blocks per wavefront
   static constexpr int W_BYTES = BN * kRowBytes;    // LDS bytes of a weight stage
   static constexpr int X_BYTES = BM * kRowBytes;    // LDS bytes of an activation stage
   static constexpr int STAGE = W_BYTES + X_BYTES;
@@ -124,58 +129,41 @@ struct LoadPlan {
   }
 };
 
-// Fragment of 32 rows x 16 k for the 32x32x16 instruction: lane l takes row
-// (l & 31) and k = ks*16 + (l >> 5)*8 .. +7 -- the same k mapping for both
-// operands, so the instruction pairs matching k.
-__device__ __forceinline__ bf16x8 read_frag(const char *lds, int row, int ks, int lane) {
-  const int lc = ks * 2 + (lane >> 5);
+// Fragment of 16 rows x 32 k for the 16x16x32 instruction: lane l takes row
+// (l & 15) and k = 8 (l >> 4) .. +7 of the step -- the same k mapping for both
+// operands, so the instruction pairs matching k.  A 32-k LDS row holds one
+// step.
+__device__ __forceinline__ bf16x8 read_frag(const char *lds, int row, int lane) {
+  const int lc = lane >> 4;
   const int off = row * kRowBytes + ((lc ^ swz(row)) << 4);
   return *reinterpret_cast<const bf16x8 *>(lds + off);
 }
 
 template <int BN, int BM>
 struct Frags {
-  bf16x8 a[BN / 64], b[BM / 64];
+  bf16x8 a[BN / 32], b[BM / 32];
 };
 
 template <int BN, int BM>
-__device__ __forceinline__ void read_frags(Frags<BN, BM> &f, const char *lds, int ks, int wn, int wm,
+__device__ __forceinline__ void read_frags(Frags<BN, BM> &f, const char *lds, int wn, int wm,
                                            int lane) {
   using C = Cfg<BN, BM>;
 #pragma unroll
-  for (int i = 0; i < C::FN; ++i) f.a[i] = read_frag(lds, wn * C::WN + i * 32 + (lane & 31), ks, lane);
+  for (int i = 0; i < C::FN; ++i) f.a[i] = read_frag(lds, wn * C::WN + i * 16 + (lane & 15), lane);
 #pragma unroll
   for (int j = 0; j < C::FM; ++j)
-    f.b[j] = read_frag(lds + C::W_BYTES, wm * C::WM + j * 32 + (lane & 31), ks, lane);
+    f.b[j] = read_frag(lds + C::W_BYTES, wm * C::WM + j * 16 + (lane & 15), lane);
 }
 
+// One 32-k step of a wavefront's blocks: block (i, j) of the wavefront's
+// WN x WM sub-tile covers n in [16i, 16i + 16) and m in [16j, 16j + 16).
 template <int BN, int BM>
-__device__ __forceinline__ void mfma_step(f32x16 (&acc)[BN / 64][BM / 64], const Frags<BN, BM> &f) {
+__device__ __forceinline__ void mfma_step(f32x4 (&acc)[BN / 32][BM / 32], const Frags<BN, BM> &f) {
 #pragma unroll
-  for (int i = 0; i < BN / 64; ++i)
+  for (int i = 0; i < BN / 32; ++i)
 #pragma unroll
-    for (int j = 0; j < BM / 64; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-}
-
-// Scheduling hint for the second half of a steady-state stage: alternate the
-// matrix-core instructions with the stage's global->LDS loads, then with the
-// next stage's fragment reads, so the memory instructions issue while the
-// matrix core is busy instead of in a block in front of it.
-template <int NMFMA, int NDMA, int NREAD>
-__device__ __forceinline__ void interleave() {
-  constexpr int NMEM = NDMA + NREAD;
-  constexpr int PER = (NMEM + NMFMA - 1) / NMFMA;  // memory instructions per MFMA slot
-#pragma unroll
-  for (int i = 0; i < NMFMA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // 1 MFMA
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int t = i * PER + j;
-      if (t < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // global->LDS
-      else if (t < NMEM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    }
-  }
+    for (int j = 0; j < BM / 32; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
 template <int LPS>
@@ -189,8 +177,15 @@ __device__ __forceinline__ void wait_stages_after(int n) {
 
 // The K loop of one tile: x and w point at the first k of this tile's K range
 // and nkb stages of BK follow.  Leaves the tile's fp32 sums in acc.
+//
+// One 32-k step per stage.  Step kb starts once every wavefront holds stage
+// kb's fragments in registers and stage kb + 1 has landed (own waits, then
+// the barrier for the other wavefronts' loads); stage kb's slot then takes
+// stage kb + kStages, and stage kb + 1's fragments are read into the same
+// registers as soon as stage kb's products have taken them.  (This path only
+// serves K % 64 == 32; K % 64 == 0 takes the 64-k stages below.)
 template <int BN, int BM>
-__device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[BN / 64][BM / 64], char *lds,
+__device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[BN / 32][BM / 32], char *lds,
                                               const uint16_t *__restrict__ x,
                                               const uint16_t *__restrict__ w, int M, int N,
                                               int nkb, int64_t ldx, int64_t ldw, int m0, int n0,
@@ -205,7 +200,7 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[BN / 64][BM / 64], c
 #pragma unroll
   for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x4{};
 
   // Prologue: stages 0 .. kStages-1 in flight.
 #pragma unroll
@@ -219,50 +214,39 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[BN / 64][BM / 64], c
   wait_stages_after<C::LPS>(min(kStages - 1, nkb - 1));
   barrier_no_fence();
 
-  Frags<BN, BM> f0, f1;
-  read_frags<BN, BM>(f0, lds, 0, wn, wm, lane);
-  // Steady state (no branches inside, so the compiler's wait-count tracking
-  // sees straight-line code): stage kb computes while kb+1..kb+3 are in
-  // flight; at mid-stage, once every wavefront has its last fragments of
-  // `cur`, the barrier frees `cur` for stage kb+4.
+  Frags<BN, BM> f;
+  read_frags<BN, BM>(f, lds, wn, wm, lane);
+  // Steady state (stage kb + kStages exists; no branches inside, so the
+  // compiler's wait-count tracking sees straight-line code): stages
+  // kb+1 .. kb+3 are in flight on entry, two may stay in flight.
   int kb = 0;
   for (; kb + kStages < nkb; ++kb) {
     char *cur = lds + (kb & (kStages - 1)) * C::STAGE;
-    char *nxt = lds + ((kb + 1) & (kStages - 1)) * C::STAGE;
-    read_frags<BN, BM>(f1, cur, 1, wn, wm, lane);
-    mfma_step<BN, BM>(acc, f0);
-    interleave<C::FN * C::FM, 0, C::FN + C::FM>();
-    __builtin_amdgcn_sched_barrier(0);
+    const char *nxt = lds + ((kb + 1) & (kStages - 1)) * C::STAGE;
     wait_lgkmcnt0();
     wait_vmcnt<2 * C::LPS>();
     barrier_no_fence();
     __builtin_amdgcn_sched_barrier(0);
     pw.issue(cur, (kb + kStages) * BK, wv);
     px.issue(cur + C::W_BYTES, (kb + kStages) * BK, wv);
-    read_frags<BN, BM>(f0, nxt, 0, wn, wm, lane);
-    mfma_step<BN, BM>(acc, f1);
-    interleave<C::FN * C::FM, C::LPS, C::FN + C::FM>();
+    mfma_step<BN, BM>(acc, f);
+    read_frags<BN, BM>(f, nxt, wn, wm, lane);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // Drain: no more stages to issue.
+  // Drain: every stage issued; after kb + 1, nkb - 2 - kb stages (at most
+  // two) may still be in flight.
   for (; kb + 1 < nkb; ++kb) {
-    char *cur = lds + (kb & (kStages - 1)) * C::STAGE;
-    char *nxt = lds + ((kb + 1) & (kStages - 1)) * C::STAGE;
-    read_frags<BN, BM>(f1, cur, 1, wn, wm, lane);
-    mfma_step<BN, BM>(acc, f0);
+    const char *nxt = lds + ((kb + 1) & (kStages - 1)) * C::STAGE;
     wait_lgkmcnt0();
     wait_stages_after<C::LPS>(nkb - 2 - kb);
     barrier_no_fence();
-    read_frags<BN, BM>(f0, nxt, 0, wn, wm, lane);
-    mfma_step<BN, BM>(acc, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step<BN, BM>(acc, f);
+    read_frags<BN, BM>(f, nxt, wn, wm, lane);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  {
-    const char *cur = lds + (kb & (kStages - 1)) * C::STAGE;
-    read_frags<BN, BM>(f1, cur, 1, wn, wm, lane);
-    mfma_step<BN, BM>(acc, f0);
-    mfma_step<BN, BM>(acc, f1);
-  }
-
+  wait_lgkmcnt0();
+  mfma_step<BN, BM>(acc, f);
 }
 
 // Epilogue through LDS, so that every global store writes whole 128-byte
@@ -271,38 +255,32 @@ __device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[BN / 64][BM / 64], c
 // same moment, stall on the L2 request rate).
 //
 // Accumulator block (i, j) of a wavefront, register v, holds
-// n = 32i + 8(v/4) + 4(lane/32) + v%4 and m = 32j + lane%32 of the
-// wavefront's WN x WM sub-tile.  Each wavefront writes its sub-tile, rounded
-// to bf16, to its own LDS region as rows of m (WN bf16 = CH 16-byte chunks,
-// chunk c of row m stored at c ^ f(m)), then reads it back 16 bytes per lane,
-// eight lanes per 128-byte row segment, and stores those segments.  f spreads
-// the 32 rows of one accumulator write over the banks and gives two adjacent
-// rows disjoint chunk sets for the reads.  The caller has made the LDS free.
-template <int BN, int BM>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[BN / 64][BM / 64], char *lds,
-                                           uint16_t *y, int M, int N, int64_t ldy, int m0, int n0,
-                                           int wn, int wm, int wv, int lane) {
-  constexpr int WN = BN / 2, WM = BM / 2;
-  constexpr int CH = WN / 8;          // 16-byte chunks per LDS row
-  constexpr int ROWB = WN * 2;        // bytes per LDS row
-  constexpr int HB = CH / 2;
+// n = 16i + 4(lane/16) + v and m = 16j + lane%16 of the wavefront's WN x WM
+// sub-tile.  Each wavefront writes its sub-tile, rounded to bf16, to its own
+// LDS region `mine` as rows of m (WN bf16 = CH 16-byte chunks, chunk c of row
+// m stored at c ^ f(m)), then reads it back 16 bytes per lane, eight lanes per
+// 128-byte row segment, and stores those segments.  f spreads the 16 rows of
+// one accumulator write over the banks and gives two adjacent rows disjoint
+// chunk sets for the reads.  The caller has made the LDS free.
+template <int FN, int FM>
+__device__ __forceinline__ void store_sub(const f32x4 (&acc)[FN][FM], char *mine, uint16_t *y,
+                                          int M, int N, int64_t ldy, int m_org, int n_org,
+                                          int lane) {
+  constexpr int WN = FN * 16, WM = FM * 16;
+  constexpr int CH = WN / 8, ROWB = WN * 2, HB = CH / 2;
   static_assert(CH == 8 || CH == 16, "sub-tile width");
-  char *mine = lds + wv * (WM * ROWB);
   auto f = [](int m) { return ((m & 1) * HB) | ((m >> 1) & (HB - 1)); };
 #pragma unroll
-  for (int j = 0; j < BM / 64; ++j) {
-    const int m = j * 32 + (lane & 31);
-    char *row = mine + m * ROWB + (lane >> 5) * 8;
+  for (int j = 0; j < FM; ++j) {
+    const int m = j * 16 + (lane & 15);
+    char *row = mine + m * ROWB + ((lane >> 4) & 1) * 8;
     const int fm = f(m);
 #pragma unroll
-    for (int i = 0; i < BN / 64; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint2 o;
-        o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-        o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-        *reinterpret_cast<uint2 *>(row + (((i * 4 + q) ^ fm) << 4)) = o;
-      }
+    for (int i = 0; i < FN; ++i) {
+      uint2 o;
+      o.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+      o.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+      *reinterpret_cast<uint2 *>(row + (((i * 2 + (lane >> 5)) ^ fm) << 4)) = o;
     }
   }
   // A wavefront's LDS operations complete in order: its reads below see its
@@ -313,9 +291,20 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[BN / 64][BM / 64]
     const int r = (t / SEG) * 8 + (lane >> 3);
     const int c = (t % SEG) * 8 + (lane & 7);
     const u32x4 v = *reinterpret_cast<const u32x4 *>(mine + r * ROWB + ((c ^ f(r)) << 4));
-    const int m = m0 + wm * WM + r, n = n0 + wn * WN + c * 8;
+    const int m = m_org + r, n = n_org + c * 8;
     if (m < M && n < N) *reinterpret_cast<u32x4 *>(y + (int64_t)m * ldy + n) = v;
   }
+}
+
+// The 4-wavefront tile: wavefront wv = (wn, wm) owns the (BN/2) x (BM/2)
+// sub-tile at (wn, wm) and one LDS region of that size.
+template <int BN, int BM>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[BN / 32][BM / 32], char *lds,
+                                           uint16_t *y, int M, int N, int64_t ldy, int m0, int n0,
+                                           int wn, int wm, int wv, int lane) {
+  constexpr int WN = BN / 2, WM = BM / 2;
+  store_sub<BN / 32, BM / 32>(acc, lds + wv * (WM * WN * 2), y, M, N, ldy, m0 + wm * WM,
+                              n0 + wn * WN, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -323,20 +312,21 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[BN / 64][BM / 64]
 // matrix row and each direct-to-LDS load instruction moves 8 full lines (one
 // 128-byte L2 request per line instead of two 64-byte ones).  Two stages fit
 // the LDS at 256 x 256; stage kb + 2 is issued once every wavefront has read
-// its last fragments of stage kb.  The k order is unchanged: 16-k matrix-core
-// steps, ascending, so the bits equal the BK = 32 kernel's.
+// its last fragments of stage kb.  The k order is unchanged: 32-k matrix-core
+// steps, ascending (two per stage), so the bits equal the BK = 32 kernel's.
 constexpr int BK2 = 64;
 constexpr int kRow2 = BK2 * 2;  // 128 bytes: eight 16-byte chunks
 
-// Chunk c of LDS row r is stored at c ^ swz2(r).  A fragment read touches 32
-// consecutive rows at one logical chunk; rows r and r + 1 share a 256-byte
-// window, so 16 consecutive rows cover the 16 bank groups exactly once.
+// Chunk c of LDS row r is stored at c ^ swz2(r).  A quarter-wavefront's
+// fragment read touches 16 consecutive rows at one logical chunk; rows r and
+// r + 1 share a 256-byte window, so those 16 rows cover the 16 bank groups
+// exactly once.
 __device__ __forceinline__ int swz2(int row) { return (row >> 1) & 7; }
 
 template <int BN, int BM>
 struct Cfg2 {
   static constexpr int WN = BN / 2, WM = BM / 2;
-  static constexpr int FN = WN / 32, FM = WM / 32;
+  static constexpr int FN = WN / 16, FM = WM / 16;  // 16x16 blocks per wavefront
   static constexpr int W_BYTES = BN * kRow2;  // one weight stage
   static constexpr int X_BYTES = BM * kRow2;  // one activation stage
   static constexpr int LW = BN / 32, LX = BM / 32;  // load instructions per wavefront per stage
@@ -373,8 +363,9 @@ struct LoadPlan2 {
   }
 };
 
-__device__ __forceinline__ bf16x8 read_frag2(const char *lds, int row, int ks, int lane) {
-  const int lc = ks * 2 + (lane >> 5);
+// Fragment of step s (k = 32s .. 32s + 31 of the stage), as read_frag.
+__device__ __forceinline__ bf16x8 read_frag2(const char *lds, int row, int s, int lane) {
+  const int lc = s * 4 + (lane >> 4);
   return *reinterpret_cast<const bf16x8 *>(lds + row * kRow2 + ((lc ^ swz2(row)) << 4));
 }
 
@@ -382,13 +373,13 @@ __device__ __forceinline__ bf16x8 read_frag2(const char *lds, int row, int ks, i
 // first, then a[1], a[2], ... -- the first product waits for two reads only.
 template <int BN, int BM>
 __device__ __forceinline__ void read_frags2(Frags<BN, BM> &f, const char *wl, const char *xl,
-                                            int ks, int wn, int wm, int lane) {
+                                            int s, int wn, int wm, int lane) {
   using C = Cfg2<BN, BM>;
-  f.a[0] = read_frag2(wl, wn * C::WN + (lane & 31), ks, lane);
+  f.a[0] = read_frag2(wl, wn * C::WN + (lane & 15), s, lane);
 #pragma unroll
-  for (int j = 0; j < C::FM; ++j) f.b[j] = read_frag2(xl, wm * C::WM + j * 32 + (lane & 31), ks, lane);
+  for (int j = 0; j < C::FM; ++j) f.b[j] = read_frag2(xl, wm * C::WM + j * 16 + (lane & 15), s, lane);
 #pragma unroll
-  for (int i = 1; i < C::FN; ++i) f.a[i] = read_frag2(wl, wn * C::WN + i * 32 + (lane & 31), ks, lane);
+  for (int i = 1; i < C::FN; ++i) f.a[i] = read_frag2(wl, wn * C::WN + i * 16 + (lane & 15), s, lane);
 }
 
 // Scheduling hint: spread the NREAD fragment reads, then the NDMA loads,
@@ -408,30 +399,20 @@ __device__ __forceinline__ void interleave_even() {
   }
 }
 
-// Steps 0..2 of a stage (fragments of steps 1..3 are read while the previous
-// step multiplies), with the loads of a later stage of the operand that has
-// the ring of 3 spread over steps 0 and 1 when LOAD.  Leaves step 3's
-// fragments in f1.
+// Step 0 of a stage (the fragments of step 1 are read while it multiplies),
+// with the loads of a later stage of the operand that has the ring of 3 when
+// LOAD.  Leaves step 1's fragments in f1.
 template <int BN, int BM, int ER, bool LOAD>
-__device__ __forceinline__ void stage_head2(f32x16 (&acc)[BN / 64][BM / 64], Frags<BN, BM> &f0,
+__device__ __forceinline__ void stage_head2(f32x4 (&acc)[BN / 32][BM / 32], Frags<BN, BM> &f0,
                                             Frags<BN, BM> &f1, const char *wc, const char *xc,
                                             const LoadPlan2<ER> &pe, char *edst, int k0, int wn,
                                             int wm, int wv, int lane) {
   using C = Cfg2<BN, BM>;
-  constexpr int LE = ER / 32, H = LE / 2;
+  constexpr int LE = ER / 32;
   read_frags2<BN, BM>(f1, wc, xc, 1, wn, wm, lane);
-  if (LOAD) pe.issue(edst, k0, wv, 0, H);
+  if (LOAD) pe.issue(edst, k0, wv);
   mfma_step<BN, BM>(acc, f0);
-  interleave_even<C::FN * C::FM, LOAD ? H : 0, C::FN + C::FM>();
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags2<BN, BM>(f0, wc, xc, 2, wn, wm, lane);
-  if (LOAD) pe.issue(edst, k0, wv, H, LE);
-  mfma_step<BN, BM>(acc, f1);
-  interleave_even<C::FN * C::FM, LOAD ? LE - H : 0, C::FN + C::FM>();
-  __builtin_amdgcn_sched_barrier(0);
-  read_frags2<BN, BM>(f1, wc, xc, 3, wn, wm, lane);
-  mfma_step<BN, BM>(acc, f0);
-  interleave_even<C::FN * C::FM, 0, C::FN + C::FM>();
+  interleave_even<C::FN * C::FM, LOAD ? LE : 0, C::FN + C::FM>();
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -443,13 +424,13 @@ constexpr int wide_lds_bytes() {
 }
 
 // One operand in a ring of 3 stages, the other in a ring of 2.  In stage kb
-// the ring-of-3 operand's stage kb + 2 loads during the first steps (its slot
+// the ring-of-3 operand's stage kb + 2 loads during the first step (its slot
 // held stage kb - 1); the ring-of-2 operand's stage kb + 2 loads after the
 // end-of-stage barrier, once every wavefront has read stage kb.  Activations
 // take the ring of 3 in the full-size kernels (W3 = false); the small-M
 // split-K partials give it to the weights, whose read dominates there.
 template <int BN, int BM, bool W3>
-__device__ __forceinline__ void gemm_mainloop2(f32x16 (&acc)[BN / 64][BM / 64], char *lds,
+__device__ __forceinline__ void gemm_mainloop2(f32x4 (&acc)[BN / 32][BM / 32], char *lds,
                                                const uint16_t *__restrict__ x,
                                                const uint16_t *__restrict__ w, int M, int N,
                                                int nkb, int64_t ldx, int64_t ldw, int m0, int n0,
@@ -463,7 +444,7 @@ __device__ __forceinline__ void gemm_mainloop2(f32x16 (&acc)[BN / 64][BM / 64], 
 #pragma unroll
   for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x4{};
 
   constexpr int NW = W3 ? 3 : 2;
   // slots: current, next, free (the free slot only for the ring of 3)
@@ -533,7 +514,7 @@ __device__ __forceinline__ void wide_tile(char *lds, const uint16_t *__restrict_
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wv >> 1, wm = wv & 1;
-  f32x16 acc[C::FN][C::FM];
+  f32x4 acc[C::FN][C::FM];
   gemm_mainloop2<BN, BM, false>(acc, lds, x, w, M, N, K / BK2, ldx, ldw, m0, n0, wv, lane, K);
   barrier_no_fence();  // every wavefront is done reading the stages
   store_tile<BN, BM>(acc, lds, y, M, N, ldy, m0, n0, wn, wm, wv, lane);
@@ -587,7 +568,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int n0 = tn * BN, m0 = tm * BM;
 
-  f32x16 acc[C::FN][C::FM];
+  f32x4 acc[C::FN][C::FM];
   gemm_mainloop<BN, BM>(acc, lds, x, w, M, N, K / BK, ldx, ldw, m0, n0, wv, lane, K);
   barrier_no_fence();  // every wavefront is done reading the stages
   store_tile<BN, BM>(acc, lds, y, M, N, ldy, m0, n0, wn, wm, wv, lane);
@@ -613,7 +594,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_partial_kernel(
   const int n0 = tn * BN, m0 = tm * BM;
   const int s = blockIdx.y;
 
-  f32x16 acc[C::FN][C::FM];
+  f32x4 acc[C::FN][C::FM];
   if constexpr (WIDE)
     gemm_mainloop2<BN, BM, true>(acc, lds, x + (int64_t)s * kc, w + (int64_t)s * kc, M, N,
                                  kc / BK2, ldx, ldw, m0, n0, wv, lane, kc);
@@ -621,23 +602,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_partial_kernel(
     gemm_mainloop<BN, BM>(acc, lds, x + (int64_t)s * kc, w + (int64_t)s * kc, M, N, kc / BK, ldx,
                           ldw, m0, n0, wv, lane, kc);
 
+  // block (i, j), lane l: n = 16i + 4(l/16) .. +3, m = 16j + l%16 (N % 8 == 0,
+  // so n < N covers all four)
   float *part = ws + (int64_t)s * M * N;
 #pragma unroll
   for (int j = 0; j < C::FM; ++j) {
-    const int m = m0 + wm * C::WM + j * 32 + (lane & 31);
+    const int m = m0 + wm * C::WM + j * 16 + (lane & 15);
     if (m >= M) continue;
     float *prow = part + (int64_t)m * N;
 #pragma unroll
     for (int i = 0; i < C::FN; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * C::WN + i * 32 + q * 8 + (lane >> 5) * 4;
-        if (n < N) {
-          f32x4 o = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
-                     acc[i][j][q * 4 + 3]};
-          *reinterpret_cast<f32x4 *>(prow + n) = o;
-        }
-      }
+      const int n = n0 + wn * C::WN + i * 16 + (lane >> 4) * 4;
+      if (n < N) *reinterpret_cast<f32x4 *>(prow + n) = acc[i][j];
     }
   }
 }
@@ -687,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_combine_kernel(
 // one stage ahead), group 1 the weights (a ring of 3, two stages ahead): with
 // few rows the weights are the stream that matters, and the ring of 3 gives
 // their loads three phases to land instead of two.
-// Every accumulator still receives its 16-k steps in ascending order from one
+// Every accumulator still receives its 32-k steps in ascending order from one
 // wave, so the bits equal the 4-wave kernels'.
 //
 // Stage timing (B(i): the i-th barrier; phases between them):
@@ -697,47 +673,12 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_combine_kernel(
 //   j+1 while reading stage j (slot of j-1) and waits for it before B(2j+2);
 //   group 1 issues weight stage j+2 while reading stage j (slot of j-1) and
 //   waits for stage j+1 before B(2j+2).
-template <int FN, int FM>
-__device__ __forceinline__ void store_sub(const f32x16 (&acc)[FN][FM], char *mine, uint16_t *y,
-                                          int M, int N, int64_t ldy, int m_org, int n_org,
-                                          int lane) {
-  constexpr int WN = FN * 32, WM = FM * 32;
-  constexpr int CH = WN / 8, ROWB = WN * 2, HB = CH / 2;
-  static_assert(CH == 8 || CH == 16, "sub-tile width");
-  auto f = [](int m) { return ((m & 1) * HB) | ((m >> 1) & (HB - 1)); };
-#pragma unroll
-  for (int j = 0; j < FM; ++j) {
-    const int m = j * 32 + (lane & 31);
-    char *row = mine + m * ROWB + (lane >> 5) * 8;
-    const int fm = f(m);
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint2 o;
-        o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-        o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-        *reinterpret_cast<uint2 *>(row + (((i * 4 + q) ^ fm) << 4)) = o;
-      }
-    }
-  }
-  constexpr int SEG = CH / 8;
-#pragma unroll 4
-  for (int t = 0; t < WM / 8 * SEG; ++t) {
-    const int r = (t / SEG) * 8 + (lane >> 3);
-    const int c = (t % SEG) * 8 + (lane & 7);
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(mine + r * ROWB + ((c ^ f(r)) << 4));
-    const int m = m_org + r, n = n_org + c * 8;
-    if (m < M && n < N) *reinterpret_cast<u32x4 *>(y + (int64_t)m * ldy + n) = v;
-  }
-}
-
 template <int BN, int BM>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
     int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
   constexpr int QN = BN / 2, QM = BM / 2, WM = QM / 2;
-  constexpr int FN = QN / 32, FM = WM / 32;
+  constexpr int FN = QN / 16, FM = WM / 16;  // 16x16 blocks per wave
   constexpr int WB = BN * kRow2, XB = BM * kRow2;
   constexpr int LW = BN / 32, LX = BM / 32;
   static_assert(2 * XB + 3 * WB <= 160 * 1024, "LDS");
@@ -756,11 +697,11 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   LoadPlan2<BN> pl;  // group 0: rows of x; group 1: rows of w
   if (g == 0) pl.init(x, M, m0, M, ldx, K, q, lane);
   else pl.init(w, N, n0, N, ldw, K, q, lane);
-  f32x16 acc[FN][FM];
+  f32x4 acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{};
 
   if (g == 0) {
     pl.issue(xs0, 0, q);
@@ -781,18 +722,18 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   barrier_no_fence();
   if (g == 1) barrier_no_fence();
 
-  bf16x8 fa[4][FN], fb[4][FM];
+  bf16x8 fa[2][FN], fb[2][FM];
   for (int j = 0; j < nkb; ++j) {
     const char *xc = (j & 1) ? xs1 : xs0;
     const int js = j % 3;
     const char *wc = js == 0 ? ws0 : (js == 1 ? ws1 : ws2);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
-      for (int i = 0; i < FN; ++i) fa[ks][i] = read_frag2(wc, nw + i * 32 + (lane & 31), ks, lane);
+      for (int i = 0; i < FN; ++i) fa[st][i] = read_frag2(wc, nw + i * 16 + (lane & 15), st, lane);
 #pragma unroll
-      for (int jj = 0; jj < FM; ++jj) fb[ks][jj] = read_frag2(xc, mw + jj * 32 + (lane & 31), ks, lane);
+      for (int jj = 0; jj < FM; ++jj) fb[st][jj] = read_frag2(xc, mw + jj * 16 + (lane & 15), st, lane);
     }
     if (g == 0) {
       if (j >= 1 && j + 1 < nkb) pl.issue((j & 1) ? xs0 : xs1, (j + 1) * BK2, q);
@@ -811,12 +752,12 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
     barrier_no_fence();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int jj = 0; jj < FM; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][jj], acc[i][jj], 0, 0, 0);
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[st][i], fb[st][jj], acc[i][jj], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (g == 0) wait_vmcnt<0>();
     barrier_no_fence();

@@ -33,11 +33,15 @@ def bf16_bits_of_f32(v) -> str:
 
 def pins():
     rows = []
-    # GEMM K-order pin: one ascending pass over K = 4096, 16 k per step.
+    # GEMM K-order pin: one ascending pass over K = 4096 in matrix-core steps
+    # (32 k per bf16 16x16x32 step).  Every non-zero product falls in a step of
+    # its own for steps of 16 k as well, so the pin does not depend on which
+    # bf16 instruction form runs the pass.
     k_terms = [(0, 1.0, 1.0), (64, 1.0, 2.0 ** -8), (2112, 1.0, 2.0 ** -24),
                (4032, 1.0, 2.0 ** -24)]
-    steps = [k // 16 for k, _, _ in k_terms]
-    assert len(set(steps)) == len(steps)
+    for step in (16, 32):
+        steps = [k // step for k, _, _ in k_terms]
+        assert len(set(steps)) == len(steps)
     terms = np.array([x * w for _, x, w in k_terms], dtype=np.float32)
     asc = oracle.combine_f32(terms.reshape(-1, 1))[0]
     desc = oracle.combine_f32(terms[::-1].copy().reshape(-1, 1))[0]
