@@ -31,9 +31,19 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-ffp-contract=off", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# Per-source additions.  gemm.hip: keep matrix-core accumulators in ordinary
+# VGPRs whenever they fit.  Left to its heuristic, the compiler puts the 4x4
+# accumulator blocks of the 4-wavefront kernels in AGPRs and shuffles them
+# between register files inside the K loop; with them in VGPRs those kernels
+# measured 2-20 % faster with the same bits (the ping-pong kernel already
+# compiles that way).
+EXTRA_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = ("packed-fp32-ops", "hip-link")
     err = "\n".join(ln for ln in r.stderr.splitlines() if not any(n in ln for n in noise))

@@ -530,30 +530,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
   wide_tile<BN, BM>(lds, x, w, y, M, N, K, ldx, ldw, ldy, tm * BM, tn * BN);
 }
 
-// 256 x 256 tiles whose last, partly filled wave is split in two along M: the
-// first nfull launch indices take whole tiles (logical tiles 0 .. nfull-1),
-// the rest take 256 x 128 halves of the remaining logical tiles, two launch
-// indices per tile.  Both shapes run the same matrix-core steps in the same
-// order, so no output's bits depend on which kind of workgroup computed it.
-__global__ __launch_bounds__(kThreads, 1) void gemm_mixed_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
-    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n,
-    int nfull) {
-  __shared__ __attribute__((aligned(1024))) char lds[wide_lds_bytes<256, 256, false>()];
-  const int pid = blockIdx.x;
-  int tm, tn;
-  if (pid < nfull) {
-    group_tile(xcd_lid(pid, nfull), tiles_m, tiles_n, tm, tn);
-    wide_tile<256, 256>(lds, x, w, y, M, N, K, ldx, ldw, ldy, tm * 256, tn * 256);
-  } else {
-    const int q = pid - nfull;
-    group_tile(nfull + (q >> 1), tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * 256 + (q & 1) * 128;
-    if (m0 >= M) return;  // the empty lower half of the last tile row
-    wide_tile<256, 128>(lds, x, w, y, M, N, K, ldx, ldw, ldy, m0, tn * 256);
-  }
-}
-
 template <int BN, int BM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
@@ -809,13 +785,13 @@ int config_for(int64_t N, int64_t K) {
 
 // Tile for bi_gemm_fill: the configuration with the smallest estimated time,
 // (waves of tiles over the CUs) x (relative time of one tile).  The tile
-// costs are measured ones, relative to 256 x 256: a 256 x 128 or 128 x 256
-// tile takes ~0.6 of it, a 128 x 128 tile ~0.34.  Ties keep the larger tile.
-// kMixed: 256 x 256 tiles with the last wave split into 256 x 128 halves
-// (gemm_mixed_kernel); only for 64-k stages.
-constexpr int kMixed = kNumConfigs;
+// costs are measured ones, relative to 256 x 256: a 256 x 128 tile takes
+// ~0.68 of it, a 128 x 256 tile ~0.67, a 128 x 128 tile ~0.34 (so three
+// waves of either half-size tile do not replace two of the big tile, which
+// measured 1-9 % slower).  Ties keep the larger tile.
 int fill_config_for(int64_t M, int64_t N, int64_t K) {
-  static const double kTileCost[kNumConfigs] = {1.0, 0.6, 0.34, 0.58};
+  (void)K;
+  static const double kTileCost[kNumConfigs] = {1.0, 0.68, 0.34, 0.67};
   const int64_t cus = cu_count();
   int best = 0;
   double best_t = 0.0;
@@ -827,17 +803,6 @@ int fill_config_for(int64_t M, int64_t N, int64_t K) {
       best = c;
       best_t = t;
     }
-  }
-  // The mixed launch, when the 256 x 256 tiles leave a last wave at most half
-  // full after one or two whole waves: whole waves of tiles, then one wave of
-  // halves.  After three or more whole waves it measured within a few percent
-  // of the plain launch either way (a partly filled last wave runs at a
-  // higher clock under the power limit), so it is not used there.
-  const int64_t T = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t r = T % cus;
-  if (K % BK2 == 0 && T > cus && T < 3 * cus && r > 0 && 2 * r <= cus) {
-    const double t = (double)(T / cus) + kTileCost[1];
-    if (t < best_t - 1e-9) best = kMixed;
   }
   return best;
 }
@@ -935,16 +900,7 @@ extern "C" int bi_gemm_fill(const uint16_t *x, const uint16_t *w, uint16_t *y, i
                             void *stream) {
   const int st = validate(x, w, y, M, N, K, ldx, ldw, ldy);
   if (st != BI_OK || M == 0) return st;
-  const int cfg = fill_config_for(M, N, K);
-  if (cfg != kMixed) return launch(cfg, x, w, y, M, N, K, ldx, ldw, ldy, stream);
-  const int64_t tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256, T = tiles_m * tiles_n;
-  const int64_t nfull = T - T % cu_count();
-  const int64_t grid = nfull + 2 * (T - nfull);
-  if (grid > 0x7FFFFFFF) return BI_ERR_SHAPE;
-  hipLaunchKernelGGL(gemm_mixed_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
-                     (hipStream_t)stream, x, w, y, (int)M, (int)N, (int)K, ldx, ldw, ldy,
-                     (int)tiles_m, (int)tiles_n, (int)nfull);
-  return launch_status();
+  return launch(fill_config_for(M, N, K), x, w, y, M, N, K, ldx, ldw, ldy, stream);
 }
 
 extern "C" int bi_gemm_with_config(int config, const uint16_t *x, const uint16_t *w, uint16_t *y,

@@ -185,16 +185,13 @@ def test_gemm_fill_validation_and_choice(lib):
     c = lib.bi_gemm_fill_config_id
     assert c(0, 4096, 4096) == -1 and c(4, 4100, 4096) == -1 and c(4, 4096, 100) == -1
     # with 256 CUs (the count assumed when no device answers): the big tile
-    # once it fills the chip, smaller ones below, and the mixed launch (id
-    # bi_gemm_num_configs()) when the big tiles make one or two whole waves
-    # and a last one at most half full
+    # once it fills the chip, smaller ones below, and never an id outside
+    # bi_gemm_with_config's range
     if c(4096, 4096, 4096) == 0:
-        mixed = lib.bi_gemm_num_configs()
         assert c(2048, 4096, 4096) == 3 and c(1000, 4096, 4096) == 2
         assert c(4096, 14336, 4096) == 0 and c(2048, 14336, 4096) == 0
-        assert c(2305, 14336, 4096) == mixed and c(4200, 4096, 4096) == mixed
-        assert c(2305, 14336, 4064) != mixed  # the mixed launch needs K % 64 == 0
-        assert c(6144, 28672, 8192) == 0  # ten whole waves: no split
+        assert c(2305, 14336, 4096) == 0 and c(4200, 4096, 4096) == 2
+        assert c(6144, 28672, 8192) == 0  # ten whole waves of the big tile
         assert c(8192, 1024, 4096) == 3 and c(4096, 1024, 4096) == 2
 
 

@@ -214,8 +214,8 @@ def test_gemm_wide_and_narrow_stages_agree(bi, K):
 def test_gemm_fill_same_bits_as_bi_gemm(bi):
     """bi_gemm_fill picks its tile from M; every tile runs the same reduction
     order, so its bits equal bi_gemm's at every M and every projection, and
-    rows stay batch-invariant across the sweep.  M = 2305 and 4200 take the
-    mixed launch with an empty lower half in the last tile row."""
+    rows stay batch-invariant across the sweep.  M = 2305 and 4200 end in a
+    partly filled tile row."""
     from invariant_deterministic_amd import harness
     c = workloads.LLAMA8B
     for si, (K, N) in enumerate(c["shapes"]):
