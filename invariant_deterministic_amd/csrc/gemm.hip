@@ -753,10 +753,10 @@ struct CfgEntry {
   int wide_threads;   // workgroup size of `wide`
 };
 
-// The 256 x 256 tile's 64-k kernel is the 8-wavefront ping-pong one.  Under
-// full load the card runs at its power limit and the 4-wavefront kernel does
-// as well; with fewer tiles than compute units (for example M = 2048 at
-// N = 4096) the ping-pong kernel's busier matrix cores pay off.
+// The 256 x 256 tile's 64-k kernel is the 8-wavefront ping-pong one.  The
+// 4-wavefront form measured 15-20 % slower: its 256 accumulators per
+// wavefront fill every AGPR, and the compiler then copies them between
+// register files inside the K loop.
 const CfgEntry kConfigs[] = {
     {256, 256, gemm_kernel<256, 256>, gemm_pp_kernel<256, 256>, 512},
     {256, 128, gemm_kernel<256, 128>, gemm_wide_kernel<256, 128>, kThreads},
