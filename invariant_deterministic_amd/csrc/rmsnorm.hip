@@ -3,8 +3,8 @@
 // "Cómo superar la no determinación en la inferencia de LLM", section
 // "RMSNorm": the batch-invariant form is data-parallel, each batch row reduced
 // by one core with the same strategy at every batch size.  Here one workgroup
-// (4 wavefronts of 64 lanes) owns one row; the order of its sum of squares
-// depends on K alone.  The page's split reduction for very small batches is
+// (4 wavefronts of 64 lanes, or one wavefront playing those four) owns one
+// row; the order of its sum of squares depends on K alone.  The page's split reduction for very small batches is
 // deliberately absent: it is the very change of strategy with batch size that
 // breaks invariance.
 //
@@ -23,6 +23,13 @@ template <int V>
 struct IntC {
   static constexpr int value = V;
 };
+
+// x + (x moved across lanes by the DPP control CTRL), all rows and banks on.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x, IntC<CTRL>) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                   0xF, 0xF, false));
+}
 
 // NCH: 16-byte chunks a thread may own (1, 2, 4 or 8), picked from K alone so
 // that the registers fit the row and nothing about the reduction changes.
@@ -89,11 +96,6 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
   // (i ^ 4) ^ 8, which hold the same value by then; offsets 2 and 1 exact
   // quad permutations.  The rows of a workgroup go through each step
   // together.
-  auto dpp_add = [](float x, auto ctrl) {
-    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                            0, __builtin_bit_cast(int, x), decltype(ctrl)::value,
-                                            0xF, 0xF, false));
-  };
 #pragma unroll
   for (int off = 32; off >= 16; off >>= 1)
 #pragma unroll
@@ -134,14 +136,102 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
   }
 }
 
+// The same rows with one 64-lane wavefront per row (a workgroup of one
+// wavefront): lane l plays threads l, l + 64, l + 128 and l + 192 of the
+// 256-thread kernel above -- virtual wavefront v = 0..3 -- with the same
+// chunks, the same per-thread sums in the same order, the same butterfly per
+// virtual wavefront, and ((s0 + s1) + s2) + s3 across them, in registers
+// instead of through LDS.  So every row's bits equal the 256-thread kernel's.
+// No barrier: each wavefront stores its row as soon as its own loads are
+// back, which lets loads and stores of different rows overlap like a copy's.
 template <int NCH>
-void launch_rows(int64_t M, int rpw, hipStream_t st, const uint16_t *x, const uint16_t *w,
+__global__ __launch_bounds__(64) void rmsnorm_wave_kernel(
+    const uint16_t *x, const uint16_t *__restrict__ w, uint16_t *y, int M, int K, int64_t ldx,
+    int64_t ldy, float eps) {
+  const int l = threadIdx.x;
+  const int nchunks = K >> 3;
+  const int row = blockIdx.x;
+  const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + (int64_t)row * ldx);
+  const u32x4 *wr = reinterpret_cast<const u32x4 *>(w);
+  u32x4 v[4][NCH], wv[4][NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = l + 64 * q + kThreads * i;  // chunk of virtual thread l + 64 q
+      if (c < nchunks) v[q][i] = __builtin_nontemporal_load(xr + c);
+    }
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = l + 64 * q + kThreads * i;
+      if (c < nchunks) wv[q][i] = wr[c];
+    }
+  float ss[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    ss[q] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = l + 64 * q + kThreads * i;
+      if (c < nchunks) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a = lo_bf16(v[q][i][j]);
+          const float b = hi_bf16(v[q][i][j]);
+          ss[q] = ss[q] + a * a;
+          ss[q] = ss[q] + b * b;
+        }
+      }
+    }
+  }
+  // the butterfly of the 256-thread kernel, once per virtual wavefront
+#pragma unroll
+  for (int off = 32; off >= 16; off >>= 1)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ss[q] = ss[q] + __shfl_xor(ss[q], off, 64);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ss[q] = dpp_add(ss[q], IntC<0x128>{});  // row_ror:8
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ss[q] = dpp_add(ss[q], IntC<0x124>{});  // row_ror:4
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ss[q] = dpp_add(ss[q], IntC<0x4E>{});   // quad_perm [2,3,0,1]
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ss[q] = dpp_add(ss[q], IntC<0xB1>{});   // quad_perm [1,0,3,2]
+  const float total = ((ss[0] + ss[1]) + ss[2]) + ss[3];
+  const float r = 1.0f / sqrtf(total / (float)K + eps);
+  u32x4 *yr = reinterpret_cast<u32x4 *>(y + (int64_t)row * ldy);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = l + 64 * q + kThreads * i;
+      if (c < nchunks) {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = (lo_bf16(v[q][i][j]) * r) * lo_bf16(wv[q][i][j]);
+          const float hi = (hi_bf16(v[q][i][j]) * r) * hi_bf16(wv[q][i][j]);
+          o[j] = pack_bf16x2(lo, hi);
+        }
+        __builtin_nontemporal_store(o, yr + c);
+      }
+    }
+}
+
+// shape: 0 = one wavefront per row, else rows per 256-thread workgroup (1 or 4)
+template <int NCH>
+void launch_rows(int64_t M, int shape, hipStream_t st, const uint16_t *x, const uint16_t *w,
                  uint16_t *y, int K, int64_t ldx, int64_t ldy, float eps) {
-  const dim3 grid((unsigned)((M + rpw - 1) / rpw)), block(kThreads);
-  if (rpw == 4)
+  if (shape == 0) {
+    hipLaunchKernelGGL((rmsnorm_wave_kernel<NCH>), dim3((unsigned)M), dim3(64), 0, st, x, w, y,
+                       (int)M, K, ldx, ldy, eps);
+    return;
+  }
+  const dim3 grid((unsigned)((M + shape - 1) / shape)), block(kThreads);
+  if (shape == 4)
     hipLaunchKernelGGL((rmsnorm_kernel<NCH, 4>), grid, block, 0, st, x, w, y, (int)M, K, ldx, ldy, eps);
-  else if (rpw == 2)
-    hipLaunchKernelGGL((rmsnorm_kernel<NCH, 2>), grid, block, 0, st, x, w, y, (int)M, K, ldx, ldy, eps);
   else
     hipLaunchKernelGGL((rmsnorm_kernel<NCH, 1>), grid, block, 0, st, x, w, y, (int)M, K, ldx, ldy, eps);
 }
@@ -166,16 +256,25 @@ extern "C" int bi_rmsnorm(const uint16_t *x, const uint16_t *w, uint16_t *y,
   if ((!in_place && overlap(sx, sy)) || overlap(sw, sy)) return BI_ERR_ALIAS;
   if (M == 0) return BI_OK;
   const int nch = (int)((K / 8 + kThreads - 1) / kThreads);
-  // Rows per workgroup: up to 4096 rows, enough rows per workgroup for about
-  // 1024 workgroups (more rows in flight per CU than one row per workgroup
-  // gives; measured at K = 4096: M = 2048: 7.5 -> 7.0 us, M = 4096: 13.8 ->
-  // 11.7 us, the copy rate of those bytes); above, one row per workgroup.
-  // Only rows with K <= 4096 (two chunks a thread) take more than one.
-  int rpw = 1;
-  if (nch <= 2 && M <= 4096) rpw = M >= 4096 ? 4 : (M >= 2048 ? 2 : 1);
+  // Launch shape from the rows per CU, for K <= 4096 (two chunks a thread);
+  // every shape gives the same bits.  Measured at K = 4096 (graph-timed,
+  // inputs rotated), per 256 CUs: one wavefront per row from 6 to 12 rows per
+  // CU (M = 2048: 7.3 -> 6.3 us against two rows per 256-thread workgroup;
+  // M = 2560: 8.4 -> 7.8), four rows per workgroup from 12 to 16 (M = 3072:
+  // 9.2 us against 10.0 for one wavefront per row; M = 4096: 11.7 against
+  // 14.0), one row per workgroup elsewhere (below, one wavefront per row
+  // measured 4-12 % slower; above 16, level or slower).  At K <= 2048 one
+  // wavefront per row lost below 8 rows per CU (M = 1536: 3.9 against 3.6 us)
+  // and gained 4-9 % from 8 to 12.
+  int shape = 1;
+  if (nch <= 2) {
+    const int64_t cus = cu_count();
+    if (M >= (nch == 2 ? 6 : 8) * cus && M < 12 * cus) shape = 0;
+    else if (M >= 12 * cus && M <= 16 * cus) shape = 4;
+  }
   hipStream_t st = (hipStream_t)stream;
-  if (nch <= 1) launch_rows<1>(M, rpw, st, x, w, y, (int)K, ldx, ldy, eps);
-  else if (nch <= 2) launch_rows<2>(M, rpw, st, x, w, y, (int)K, ldx, ldy, eps);
+  if (nch <= 1) launch_rows<1>(M, shape, st, x, w, y, (int)K, ldx, ldy, eps);
+  else if (nch <= 2) launch_rows<2>(M, shape, st, x, w, y, (int)K, ldx, ldy, eps);
   else if (nch <= 4) launch_rows<4>(M, 1, st, x, w, y, (int)K, ldx, ldy, eps);
   else launch_rows<8>(M, 1, st, x, w, y, (int)K, ldx, ldy, eps);
   return launch_status();

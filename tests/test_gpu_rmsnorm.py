@@ -54,8 +54,9 @@ def test_rmsnorm_batch_invariance_prefix_permuted_reruns(bi):
     run = lambda xb: bi.bi_rmsnorm(xb, Wt, eps=workloads.EPS)
     perm = torch.from_numpy(synth.permutation(x.shape[0], c["perm_seed"]))
     probes = [0, 1, 6, 7, 127, 128, 2047, 4095, 8191] + list(range(200, 8192, 997))
-    # beyond the configured sizes: 3000 and 4096 run two and four rows per
-    # workgroup, 4097 one again, so rows meet every workgroup shape
+    # beyond the configured sizes (256 CUs): 2048 and 3000 run one wavefront
+    # per row, 4096 four rows per workgroup, 4097 and 8192 one row per
+    # 256-thread workgroup, so rows meet every launch shape
     batches = harness.prefix_and_permuted_batches(tuple(c["Ms"]) + (3000, 4096, 4097), x.shape[0],
                                                   perm, "cuda")
     say("rmsnorm batch invariance")
@@ -77,6 +78,28 @@ def test_rmsnorm_ragged_k_and_limits(bi):
         for i in range(M):
             yi = host_u16(bi.bi_rmsnorm(dev_bf16(x[i:i + 1]), dev_bf16(w), eps=eps))
             assert np.array_equal(yi[0], y[i])
+
+
+def test_rmsnorm_one_wavefront_per_row_ragged_k(bi):
+    """The one-wavefront-per-row launch (6-12 rows per CU at K <= 4096, 8-12 at
+    K <= 2048) on ragged K, where some lanes of a virtual wavefront own no
+    chunk: oracle parity, and every sampled row equal to the same row alone
+    (one row per 256-thread workgroup)."""
+    eps = workloads.EPS
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = synth.rng(31)
+    for K in (1032, 2056, 3080, 4096):
+        M = 10 * cus
+        say(f"rmsnorm one wavefront per row K={K} M={M}")
+        x = synth.normal_bf16((M, K), 40 + K)
+        w = synth.normal_bf16((K,), 50 + K, mean=1.0, std=0.1)
+        X, Wt = dev_bf16(x), dev_bf16(w)
+        y = host_u16(bi.bi_rmsnorm(X, Wt, eps=eps))
+        rows = np.unique(np.concatenate([[0, 1, M - 1], g.integers(0, M, size=40)]))
+        check_bf16(y[rows], oracle.rmsnorm(x[rows], w, eps), f"K={K}")
+        for i in rows[:12]:
+            yi = host_u16(bi.bi_rmsnorm(X[i:i + 1], Wt, eps=eps))
+            assert np.array_equal(yi[0], y[i]), (K, int(i))
 
 
 def test_rmsnorm_closed_forms(bi):
