@@ -144,23 +144,33 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
 // instead of through LDS.  So every row's bits equal the 256-thread kernel's.
 // No barrier: each wavefront stores its row as soon as its own loads are
 // back, which lets loads and stores of different rows overlap like a copy's.
-template <int NCH>
+// RW rows per wavefront, each with its own chunks, sums and tree (rows past
+// M, in the last wavefront only, load row M - 1 and store nothing).
+template <int NCH, int RW>
 __global__ __launch_bounds__(64) void rmsnorm_wave_kernel(
     const uint16_t *x, const uint16_t *__restrict__ w, uint16_t *y, int M, int K, int64_t ldx,
     int64_t ldy, float eps) {
   const int l = threadIdx.x;
   const int nchunks = K >> 3;
-  const int row = blockIdx.x;
-  const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + (int64_t)row * ldx);
+  const int row0 = blockIdx.x * RW;
   const u32x4 *wr = reinterpret_cast<const u32x4 *>(w);
-  u32x4 v[4][NCH], wv[4][NCH];
+  u32x4 v[RW][4][NCH], wv[4][NCH];
 #pragma unroll
-  for (int i = 0; i < NCH; ++i)
+  for (int rr = 0; rr < RW; ++rr) {
+    // (with one row per wavefront the grid has exactly M wavefronts; the
+    // clamp and the store guard below are left out there: measured, their
+    // code alone cost 10 % at M = 2048)
+    int row = row0 + rr;
+    if constexpr (RW > 1) row = row < M ? row : M - 1;
+    const u32x4 *xr = reinterpret_cast<const u32x4 *>(x + (int64_t)row * ldx);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = l + 64 * q + kThreads * i;  // chunk of virtual thread l + 64 q
-      if (c < nchunks) v[q][i] = __builtin_nontemporal_load(xr + c);
-    }
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = l + 64 * q + kThreads * i;  // chunk of virtual thread l + 64 q
+        if (c < nchunks) v[rr][q][i] = __builtin_nontemporal_load(xr + c);
+      }
+  }
 #pragma unroll
   for (int i = 0; i < NCH; ++i)
 #pragma unroll
@@ -168,66 +178,92 @@ __global__ __launch_bounds__(64) void rmsnorm_wave_kernel(
       const int c = l + 64 * q + kThreads * i;
       if (c < nchunks) wv[q][i] = wr[c];
     }
-  float ss[4];
+  float ss[RW][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    ss[q] = 0.0f;
+  for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = l + 64 * q + kThreads * i;
-      if (c < nchunks) {
+    for (int q = 0; q < 4; ++q) {
+      ss[rr][q] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float a = lo_bf16(v[q][i][j]);
-          const float b = hi_bf16(v[q][i][j]);
-          ss[q] = ss[q] + a * a;
-          ss[q] = ss[q] + b * b;
+      for (int i = 0; i < NCH; ++i) {
+        const int c = l + 64 * q + kThreads * i;
+        if (c < nchunks) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float a = lo_bf16(v[rr][q][i][j]);
+            const float b = hi_bf16(v[rr][q][i][j]);
+            ss[rr][q] = ss[rr][q] + a * a;
+            ss[rr][q] = ss[rr][q] + b * b;
+          }
         }
       }
     }
-  }
-  // the butterfly of the 256-thread kernel, once per virtual wavefront
+  // the butterfly of the 256-thread kernel, once per virtual wavefront and row
 #pragma unroll
   for (int off = 32; off >= 16; off >>= 1)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ss[q] = ss[q] + __shfl_xor(ss[q], off, 64);
+    for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ss[q] = dpp_add(ss[q], IntC<0x128>{});  // row_ror:8
+      for (int q = 0; q < 4; ++q) ss[rr][q] = ss[rr][q] + __shfl_xor(ss[rr][q], off, 64);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ss[q] = dpp_add(ss[q], IntC<0x124>{});  // row_ror:4
+  for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ss[q] = dpp_add(ss[q], IntC<0x4E>{});   // quad_perm [2,3,0,1]
+    for (int q = 0; q < 4; ++q) ss[rr][q] = dpp_add(ss[rr][q], IntC<0x128>{});  // row_ror:8
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ss[q] = dpp_add(ss[q], IntC<0xB1>{});   // quad_perm [1,0,3,2]
-  const float total = ((ss[0] + ss[1]) + ss[2]) + ss[3];
-  const float r = 1.0f / sqrtf(total / (float)K + eps);
-  u32x4 *yr = reinterpret_cast<u32x4 *>(y + (int64_t)row * ldy);
+  for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
-  for (int i = 0; i < NCH; ++i)
+    for (int q = 0; q < 4; ++q) ss[rr][q] = dpp_add(ss[rr][q], IntC<0x124>{});  // row_ror:4
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = l + 64 * q + kThreads * i;
-      if (c < nchunks) {
-        u32x4 o;
+  for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float lo = (lo_bf16(v[q][i][j]) * r) * lo_bf16(wv[q][i][j]);
-          const float hi = (hi_bf16(v[q][i][j]) * r) * hi_bf16(wv[q][i][j]);
-          o[j] = pack_bf16x2(lo, hi);
-        }
-        __builtin_nontemporal_store(o, yr + c);
-      }
+    for (int q = 0; q < 4; ++q) ss[rr][q] = dpp_add(ss[rr][q], IntC<0x4E>{});  // quad_perm [2,3,0,1]
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ss[rr][q] = dpp_add(ss[rr][q], IntC<0xB1>{});  // quad_perm [1,0,3,2]
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr) {
+    if constexpr (RW > 1) {
+      if (row0 + rr >= M) break;
     }
+    const float total = ((ss[rr][0] + ss[rr][1]) + ss[rr][2]) + ss[rr][3];
+    const float r = 1.0f / sqrtf(total / (float)K + eps);
+    u32x4 *yr = reinterpret_cast<u32x4 *>(y + (int64_t)(row0 + rr) * ldy);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = l + 64 * q + kThreads * i;
+        if (c < nchunks) {
+          u32x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float lo = (lo_bf16(v[rr][q][i][j]) * r) * lo_bf16(wv[q][i][j]);
+            const float hi = (hi_bf16(v[rr][q][i][j]) * r) * hi_bf16(wv[q][i][j]);
+            o[j] = pack_bf16x2(lo, hi);
+          }
+          __builtin_nontemporal_store(o, yr + c);
+        }
+      }
+  }
 }
 
-// shape: 0 = one wavefront per row, else rows per 256-thread workgroup (1 or 4)
+// shape: -1 / -4 = one / four rows per 64-lane wavefront, 1 / 4 = rows per
+// 256-thread workgroup
 template <int NCH>
 void launch_rows(int64_t M, int shape, hipStream_t st, const uint16_t *x, const uint16_t *w,
                  uint16_t *y, int K, int64_t ldx, int64_t ldy, float eps) {
-  if (shape == 0) {
-    hipLaunchKernelGGL((rmsnorm_wave_kernel<NCH>), dim3((unsigned)M), dim3(64), 0, st, x, w, y,
-                       (int)M, K, ldx, ldy, eps);
-    return;
+  if constexpr (NCH <= 2) {
+    if (shape == -1) {
+      hipLaunchKernelGGL((rmsnorm_wave_kernel<NCH, 1>), dim3((unsigned)M), dim3(64), 0, st, x, w,
+                         y, (int)M, K, ldx, ldy, eps);
+      return;
+    }
+    if (shape == -4) {
+      hipLaunchKernelGGL((rmsnorm_wave_kernel<NCH, 4>), dim3((unsigned)((M + 3) / 4)), dim3(64), 0,
+                         st, x, w, y, (int)M, K, ldx, ldy, eps);
+      return;
+    }
   }
   const dim3 grid((unsigned)((M + shape - 1) / shape)), block(kThreads);
   if (shape == 4)
@@ -257,20 +293,27 @@ extern "C" int bi_rmsnorm(const uint16_t *x, const uint16_t *w, uint16_t *y,
   if (M == 0) return BI_OK;
   const int nch = (int)((K / 8 + kThreads - 1) / kThreads);
   // Launch shape from the rows per CU, for K <= 4096 (two chunks a thread);
-  // every shape gives the same bits.  Measured at K = 4096 (graph-timed,
-  // inputs rotated), per 256 CUs: one wavefront per row from 6 to 12 rows per
-  // CU (M = 2048: 7.3 -> 6.3 us against two rows per 256-thread workgroup;
-  // M = 2560: 8.4 -> 7.8), four rows per workgroup from 12 to 16 (M = 3072:
-  // 9.2 us against 10.0 for one wavefront per row; M = 4096: 11.7 against
-  // 14.0), one row per workgroup elsewhere (below, one wavefront per row
-  // measured 4-12 % slower; above 16, level or slower).  At K <= 2048 one
-  // wavefront per row lost below 8 rows per CU (M = 1536: 3.9 against 3.6 us)
-  // and gained 4-9 % from 8 to 12.
+  // every shape gives the same bits.  The one-wavefront kernels do best when
+  // every wavefront of the launch is resident at once, at 6-8 wavefronts per
+  // CU.  Measured at K = 4096 (graph-timed, inputs rotated), per 256 CUs:
+  //   6-12 rows per CU: one row per wavefront (M = 2048: 6.3 us against 7.2
+  //     for the best 256-thread shape; M = 2560: 7.8 against 8.4);
+  //   12-16: four rows per 256-thread workgroup (M = 3072: 9.2 us against
+  //     10.0 for one row per wavefront; M = 4096: 11.7 against 14.0);
+  //   16-32: four rows per wavefront (M = 6144: 17.4 us against 18.9;
+  //     M = 8192: 22.0-22.3 against 23.6-24.1 on three boxes; above 32 rows
+  //     per CU its wavefronts no longer fit at once and it lost 6-17 %);
+  //   elsewhere one row per 256-thread workgroup (below 6 rows per CU one
+  //     row per wavefront measured 4-12 % slower).
+  // At K <= 2048, one row per wavefront lost below 8 rows per CU (M = 1536:
+  // 3.9 against 3.6 us) and gained 4-9 % from 8 to 12; four rows per
+  // wavefront is only used at K > 2048, where it was measured.
   int shape = 1;
   if (nch <= 2) {
     const int64_t cus = cu_count();
-    if (M >= (nch == 2 ? 6 : 8) * cus && M < 12 * cus) shape = 0;
+    if (M >= (nch == 2 ? 6 : 8) * cus && M < 12 * cus) shape = -1;
     else if (M >= 12 * cus && M <= 16 * cus) shape = 4;
+    else if (nch == 2 && M > 16 * cus && M <= 32 * cus) shape = -4;
   }
   hipStream_t st = (hipStream_t)stream;
   if (nch <= 1) launch_rows<1>(M, shape, st, x, w, y, (int)K, ldx, ldy, eps);

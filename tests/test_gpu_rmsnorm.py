@@ -54,9 +54,10 @@ def test_rmsnorm_batch_invariance_prefix_permuted_reruns(bi):
     run = lambda xb: bi.bi_rmsnorm(xb, Wt, eps=workloads.EPS)
     perm = torch.from_numpy(synth.permutation(x.shape[0], c["perm_seed"]))
     probes = [0, 1, 6, 7, 127, 128, 2047, 4095, 8191] + list(range(200, 8192, 997))
-    # beyond the configured sizes (256 CUs): 2048 and 3000 run one wavefront
-    # per row, 4096 four rows per workgroup, 4097 and 8192 one row per
-    # 256-thread workgroup, so rows meet every launch shape
+    # beyond the configured sizes (256 CUs): 1, 7 and 128 run one row per
+    # 256-thread workgroup, 2048 and 3000 one row per wavefront, 4096 four rows
+    # per workgroup, 4097 and 8192 four rows per wavefront (4097 with a partly
+    # filled last wavefront), so rows meet every launch shape
     batches = harness.prefix_and_permuted_batches(tuple(c["Ms"]) + (3000, 4096, 4097), x.shape[0],
                                                   perm, "cuda")
     say("rmsnorm batch invariance")
@@ -80,16 +81,18 @@ def test_rmsnorm_ragged_k_and_limits(bi):
             assert np.array_equal(yi[0], y[i])
 
 
-def test_rmsnorm_one_wavefront_per_row_ragged_k(bi):
-    """The one-wavefront-per-row launch (6-12 rows per CU at K <= 4096, 8-12 at
-    K <= 2048) on ragged K, where some lanes of a virtual wavefront own no
-    chunk: oracle parity, and every sampled row equal to the same row alone
-    (one row per 256-thread workgroup)."""
+@pytest.mark.parametrize("rows_per_cu", [10, 20])
+def test_rmsnorm_one_wavefront_launches_ragged_k(bi, rows_per_cu):
+    """The one-wavefront launches -- one row per wavefront at 6-12 rows per CU
+    (8-12 at K <= 2048), four rows per wavefront at 16-32 (K > 2048) -- on
+    ragged K, where some lanes of a virtual wavefront own no chunk, and with a
+    partly filled last wavefront: oracle parity, and every sampled row equal
+    to the same row alone (one row per 256-thread workgroup)."""
     eps = workloads.EPS
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    g = synth.rng(31)
-    for K in (1032, 2056, 3080, 4096):
-        M = 10 * cus
+    g = synth.rng(31 + rows_per_cu)
+    for K in ((1032, 2056, 3080, 4096) if rows_per_cu == 10 else (2056, 3080, 4096)):
+        M = rows_per_cu * cus + (3 if rows_per_cu == 20 else 0)
         say(f"rmsnorm one wavefront per row K={K} M={M}")
         x = synth.normal_bf16((M, K), 40 + K)
         w = synth.normal_bf16((K,), 50 + K, mean=1.0, std=0.1)
