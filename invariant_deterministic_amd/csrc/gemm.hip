@@ -624,6 +624,122 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_combine_kernel(
   *reinterpret_cast<u32x2 *>(y + m * ldy + n) = o;
 }
 
+// Split-K in one launch for batches of at most 16 rows.  A workgroup owns 16
+// output columns and every chunk of K; wavefront wv takes chunks wv, wv + nw,
+// ... one after another.  Each chunk is the same ascending run of 32-k
+// matrix-core steps from zero as in gemm_partial_kernel (the weight and
+// activation rows fetched as whole 128-byte lines and moved into the
+// matrix-core layout in registers), so every partial p_s has the same bits.
+// p_s goes to the workspace, as there, and to LDS; once every chunk is in, one
+// wavefront folds ((p_0 + p_1) + ...) + p_{S-1} in fp32 and rounds once, as
+// gemm_splitk_combine_kernel does.  At these sizes the separate fold's launch
+// and the round trip of the partials through memory cost about as much as the
+// weight stream itself.
+constexpr int kFusedMaxM = 16;
+constexpr int kFusedGroupK = 128;  // k per fetch group: two line pairs, four 32-k steps
+constexpr int kFusedMaxWaves = 16;
+constexpr int kFusedMaxChunks = 64 / kFusedMaxWaves;  // per wavefront (split_k <= 64)
+
+__device__ __forceinline__ void fused_group(const LineOperand16<2, true> &wl,
+                                            const LineOperand16<2, false> &xl, f32x4 &acc,
+                                            bool first, int lane) {
+  bf16x8 fw[4], fx[4];
+  wl.place(fw, lane);
+  xl.place(fx, lane);
+  if (first) acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[t], fx[t], acc, 0, 0, 0);
+}
+
+// (x and w are not __restrict__: the compiler may then move their loads
+// across the empty asm statement that keeps them ahead of the products.)
+__global__ __launch_bounds__(64 * kFusedMaxWaves) void gemm_splitk_fused_kernel(
+    const uint16_t *x, const uint16_t *w, float *__restrict__ ws,
+    uint16_t *__restrict__ y, int M, int N, int S, int kc, int64_t ldx, int64_t ldw, int64_t ldy) {
+  extern __shared__ __attribute__((aligned(16))) float part[];  // [S][16 m][16 n]
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;  // <= S
+  const int n0 = blockIdx.x * 16;
+  // Line loads (LineOperand16): lane 8q + u fetches unit u of row q and unit
+  // u ^ 4 of row 8 + q.  Rows past the matrix edge repeat its last row; their
+  // results are never stored.
+  const int q = lane >> 3, u = lane & 7;
+  const uint16_t *wlo = w + (int64_t)min(n0 + q, N - 1) * ldw + 8 * u;
+  const uint16_t *whi = w + (int64_t)min(n0 + 8 + q, N - 1) * ldw + 8 * (u ^ 4);
+  const uint16_t *xlo = x + (int64_t)min(q, M - 1) * ldx + 8 * u;
+  const uint16_t *xhi = x + (int64_t)min(8 + q, M - 1) * ldx + 8 * (u ^ 4);
+  const int gpc = kc / kFusedGroupK;            // fetch groups per chunk
+  const int nch = (S - 1 - wv) / nw + 1;        // chunks of this wavefront (at most 4)
+  const int G = nch * gpc;                      // its fetch groups
+  auto k_of = [&](int g) {
+    return (int64_t)(wv + (g / gpc) * nw) * kc + (int64_t)(g % gpc) * kFusedGroupK;
+  };
+  LineOperand16<2, true> wa, wb;
+  LineOperand16<2, false> xa, xb;
+  auto issue = [&](LineOperand16<2, true> &wl, LineOperand16<2, false> &xl, int g) {
+    const int64_t k = k_of(g);
+    wl.issue(wlo + k, whi + k);
+    xl.issue(xlo + k, xhi + k);
+    // keep these loads ahead of the products that follow them in the source:
+    // left alone, the compiler sinks them below and loses the overlap
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The chunk partials stay in registers until every load has been issued:
+  // a store inside the loop would make the compiler wait for every load.
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, ps[kFusedMaxChunks] = {};
+  auto consume = [&](const LineOperand16<2, true> &wl, const LineOperand16<2, false> &xl, int g) {
+    fused_group(wl, xl, acc, g % gpc == 0, lane);
+    const int ci = g / gpc;
+#pragma unroll
+    for (int i = 0; i < kFusedMaxChunks; ++i)
+      if (i == ci) ps[i] = acc;
+  };
+  // Two groups in flight: one loads while the other multiplies.  The loop
+  // body has no branch around a load, so the waits count exactly.
+  issue(wa, xa, 0);
+  int g = 0;
+  for (; g + 2 < G; g += 2) {
+    issue(wb, xb, g + 1);
+    consume(wa, xa, g);
+    issue(wa, xa, g + 2);
+    consume(wb, xb, g + 1);
+  }
+  if (g + 1 < G) {
+    issue(wb, xb, g + 1);
+    consume(wa, xa, g);
+    consume(wb, xb, g + 1);
+  } else {
+    consume(wa, xa, g);
+  }
+  // every chunk's partial, to LDS and to the workspace.  Block layout:
+  // register v of lane l is n = 4 (l >> 4) + v, m = l & 15.
+  {
+    const int m = lane & 15, c = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < kFusedMaxChunks; ++i) {
+      if (i >= nch) break;
+      const int s = wv + i * nw;
+      *reinterpret_cast<f32x4 *>(part + (s * 16 + m) * 16 + 4 * c) = ps[i];
+      if (m < M && n0 + 4 * c < N)
+        *reinterpret_cast<f32x4 *>(ws + ((int64_t)s * M + m) * N + n0 + 4 * c) = ps[i];
+    }
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  // lane t: row t / 4, columns 4 (t % 4) .. +3
+  const int m = lane >> 2, c = lane & 3;
+  if (m >= M || n0 + 4 * c >= N) return;
+  const float *p = part + m * 16 + 4 * c;
+  f32x4 a = *reinterpret_cast<const f32x4 *>(p);  // the fold starts from p_0 itself
+  for (int s = 1; s < S; ++s) a = a + *reinterpret_cast<const f32x4 *>(p + s * 256);
+  u32x2 o;
+  o[0] = pack_bf16x2(a[0], a[1]);
+  o[1] = pack_bf16x2(a[2], a[3]);
+  *reinterpret_cast<u32x2 *>(y + (int64_t)m * ldy + n0 + 4 * c) = o;
+}
+
 // ---------------------------------------------------------------------------
 // Ping-pong variant of the 64-k kernel: 8 wavefronts, two per SIMD (the
 // dispatcher places wave w on SIMD w & 3; only the overlap described below,
@@ -939,13 +1055,21 @@ int splitk_validate(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M
 }
 
 // The partial kernel over (tiles, split_k), then the fixed-order fold; wsf
-// holds split_k * M * N floats.
+// holds split_k * M * N floats.  Batches of at most 16 rows (chunks a multiple
+// of 128 k) take the one-launch kernel instead: same partials, same fold.
 int splitk_launch(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t N,
                   int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, int split_k, float *wsf,
                   void *stream) {
   const int64_t tiles_m = (M + kSplitBM - 1) / kSplitBM, tiles_n = (N + kSplitBN - 1) / kSplitBN;
   hipStream_t s = (hipStream_t)stream;
   const int kc = (int)(K / split_k);
+  if (M <= kFusedMaxM && kc % kFusedGroupK == 0) {
+    const int nw = split_k < kFusedMaxWaves ? split_k : kFusedMaxWaves;
+    hipLaunchKernelGGL(gemm_splitk_fused_kernel, dim3((unsigned)((N + 15) / 16)), dim3(64 * nw),
+                       (size_t)split_k * 16 * 16 * sizeof(float), s, x, w, wsf, y, (int)M, (int)N,
+                       split_k, kc, ldx, ldw, ldy);
+    return launch_status();
+  }
   if (kc % BK2 == 0)
     hipLaunchKernelGGL((gemm_partial_kernel<kSplitBN, kSplitBM, true>),
                        dim3((unsigned)(tiles_m * tiles_n), (unsigned)split_k), dim3(kThreads), 0, s,
