@@ -79,16 +79,19 @@ constexpr int kCpolNT = 2;
 //     q = lane >> 3, u = lane & 7; step pair g is read at +64g elements.
 //   place(out): out[t] for t < 2*NP in the matrix-core layout; place_pair(g,
 //     out): steps 2g, 2g + 1 only.
-template <int NP, bool NT>
+// ROWS8: only rows 0-7 are needed.  The hi loads are skipped and lo stands in
+// for hi, so rows 8-15 of the placed fragments hold other values (their
+// products must be discarded); rows 0-7 are exactly as with ROWS8 false.
+template <int NP, bool NT, bool ROWS8 = false>
 struct LineOperand16 {
-  u32x4 lo[NP], hi[NP];
+  u32x4 lo[NP], hi[ROWS8 ? 1 : NP];
   __device__ __forceinline__ void issue(const uint16_t *plo, const uint16_t *phi) {
 #pragma unroll
     for (int g = 0; g < NP; ++g) {
       const u32x4 *a = reinterpret_cast<const u32x4 *>(plo + 64 * g);
       const u32x4 *b = reinterpret_cast<const u32x4 *>(phi + 64 * g);
       lo[g] = NT ? __builtin_nontemporal_load(a) : *a;
-      hi[g] = NT ? __builtin_nontemporal_load(b) : *b;
+      if constexpr (!ROWS8) hi[g] = NT ? __builtin_nontemporal_load(b) : *b;
     }
   }
   // Step 2g, lane r + 16c (r < 8) wants unit c of row r: lo of lane 8r + c;
@@ -105,8 +108,13 @@ struct LineOperand16 {
     u32x4 t0, t1;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      t0[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src0, (int)(first ? lo[g][d] : hi[g][d]));
-      t1[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, (int)(first ? hi[g][d] : lo[g][d]));
+      if constexpr (ROWS8) {
+        t0[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src0, (int)lo[g][d]);
+        t1[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, (int)lo[g][d]);
+      } else {
+        t0[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src0, (int)(first ? lo[g][d] : hi[g][d]));
+        t1[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src1, (int)(first ? hi[g][d] : lo[g][d]));
+      }
     }
     out[0] = __builtin_bit_cast(bf16x8, t0);
     out[1] = __builtin_bit_cast(bf16x8, t1);

@@ -640,8 +640,9 @@ constexpr int kFusedGroupK = 128;  // k per fetch group: two line pairs, four 32
 constexpr int kFusedMaxWaves = 16;
 constexpr int kFusedMaxChunks = 64 / kFusedMaxWaves;  // per wavefront (split_k <= 64)
 
+template <bool ROWS8>
 __device__ __forceinline__ void fused_group(const LineOperand16<2, true> &wl,
-                                            const LineOperand16<2, false> &xl, f32x4 &acc,
+                                            const LineOperand16<2, false, ROWS8> &xl, f32x4 &acc,
                                             bool first, int lane) {
   bf16x8 fw[4], fx[4];
   wl.place(fw, lane);
@@ -653,6 +654,10 @@ __device__ __forceinline__ void fused_group(const LineOperand16<2, true> &wl,
 
 // (x and w are not __restrict__: the compiler may then move their loads
 // across the empty asm statement that keeps them ahead of the products.)
+// ROWS8 (M <= 8): only the first 8 rows of x are fetched; the products of
+// fragment rows 8-15 are then meaningless and, as always for rows >= M, never
+// stored or folded.
+template <bool ROWS8>
 __global__ __launch_bounds__(64 * kFusedMaxWaves) void gemm_splitk_fused_kernel(
     const uint16_t *x, const uint16_t *w, float *__restrict__ ws,
     uint16_t *__restrict__ y, int M, int N, int S, int kc, int64_t ldx, int64_t ldw, int64_t ldy) {
@@ -676,8 +681,8 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void gemm_splitk_fused_kernel(
     return (int64_t)(wv + (g / gpc) * nw) * kc + (int64_t)(g % gpc) * kFusedGroupK;
   };
   LineOperand16<2, true> wa, wb;
-  LineOperand16<2, false> xa, xb;
-  auto issue = [&](LineOperand16<2, true> &wl, LineOperand16<2, false> &xl, int g) {
+  LineOperand16<2, false, ROWS8> xa, xb;
+  auto issue = [&](LineOperand16<2, true> &wl, LineOperand16<2, false, ROWS8> &xl, int g) {
     const int64_t k = k_of(g);
     wl.issue(wlo + k, whi + k);
     xl.issue(xlo + k, xhi + k);
@@ -689,7 +694,7 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void gemm_splitk_fused_kernel(
   // The chunk partials stay in registers until every load has been issued:
   // a store inside the loop would make the compiler wait for every load.
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, ps[kFusedMaxChunks] = {};
-  auto consume = [&](const LineOperand16<2, true> &wl, const LineOperand16<2, false> &xl, int g) {
+  auto consume = [&](const LineOperand16<2, true> &wl, const LineOperand16<2, false, ROWS8> &xl, int g) {
     fused_group(wl, xl, acc, g % gpc == 0, lane);
     const int ci = g / gpc;
 #pragma unroll
@@ -1065,9 +1070,14 @@ int splitk_launch(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, 
   const int kc = (int)(K / split_k);
   if (M <= kFusedMaxM && kc % kFusedGroupK == 0) {
     const int nw = split_k < kFusedMaxWaves ? split_k : kFusedMaxWaves;
-    hipLaunchKernelGGL(gemm_splitk_fused_kernel, dim3((unsigned)((N + 15) / 16)), dim3(64 * nw),
-                       (size_t)split_k * 16 * 16 * sizeof(float), s, x, w, wsf, y, (int)M, (int)N,
-                       split_k, kc, ldx, ldw, ldy);
+    const dim3 grid((unsigned)((N + 15) / 16)), block(64 * nw);
+    const size_t lds = (size_t)split_k * 16 * 16 * sizeof(float);
+    if (M <= 8)
+      hipLaunchKernelGGL(gemm_splitk_fused_kernel<true>, grid, block, lds, s, x, w, wsf, y, (int)M,
+                         (int)N, split_k, kc, ldx, ldw, ldy);
+    else
+      hipLaunchKernelGGL(gemm_splitk_fused_kernel<false>, grid, block, lds, s, x, w, wsf, y, (int)M,
+                         (int)N, split_k, kc, ldx, ldw, ldy);
     return launch_status();
   }
   if (kc % BK2 == 0)
