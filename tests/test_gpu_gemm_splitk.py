@@ -99,12 +99,14 @@ def test_splitk_partials_and_exact_combine(bi):
 
 
 @pytest.mark.parametrize("M,N,K,S", [(1, 1032, 4096, 32), (16, 1032, 4096, 4), (7, 264, 14336, 8), (5, 520, 3072, 8),
-                                     (3, 4096, 2048, 16)])
+                                     (3, 4096, 2048, 16), (17, 1032, 4096, 32), (32, 264, 14336, 8),
+                                     (25, 520, 3072, 2)])
 def test_splitk_one_launch_partials_and_fold(bi, M, N, K, S):
     """Batches of at most 16 rows take the one-launch kernel (chunks folded in
-    LDS).  Its workspace still holds every partial, each matching the oracle
-    over its chunk, and y is bit-exactly the oracle's fold of them; N = 1032
-    and 264 leave the last 16-column block half full."""
+    LDS), larger ones the partial and fold kernels.  Either way the workspace
+    holds every partial, each matching the oracle over its chunk, and y is
+    bit-exactly the oracle's fold of them; N = 1032 and 264 leave the last
+    16-column block half full."""
     x = synth.normal_bf16((M, K), 307 + M)
     w = synth.normal_bf16((N, K), 308 + N, std=0.02)
     X, Wt = dev_bf16(x), dev_bf16(w)
@@ -122,28 +124,31 @@ def test_splitk_one_launch_partials_and_fold(bi, M, N, K, S):
 @pytest.mark.parametrize("shape_index", [0, 1, 2, 3])
 def test_splitk_one_launch_equals_two_launch(bi, shape_index):
     """Rows computed in batches of 1-16 (one launch) are bitwise the rows of a
-    17-row batch (partial kernel + fold kernel), at the projection's own split
-    and at the extremes of the split range, contiguous and strided."""
+    33-row batch (partial kernel + fold kernel), as are those of batches of
+    17-32, at the projection's own split and at the extremes of the split
+    range, contiguous and strided."""
     c = workloads.LLAMA8B
     K, N = c["shapes"][shape_index]
-    x = workloads.llama8b_x(K, rows=17)
+    x = workloads.llama8b_x(K, rows=33)
     w = workloads.llama8b_w(shape_index)
     X, Wt = dev_bf16(x), dev_bf16(w)
     for S in sorted({bi.bi_gemm_splitk_for(N, K), 1, 2, 64}):
         if K % (32 * S):
             continue
         ref = host_u16(bi.bi_gemm_splitk(X, Wt, split_k=S))
-        for M in (1, 2, 7, 16):
+        for M in (1, 2, 7, 16, 17, 30, 32):
             say(f"splitk one vs two launches K={K} N={N} S={S} M={M}")
             assert np.array_equal(host_u16(bi.bi_gemm_splitk(X[:M], Wt, split_k=S)), ref[:M]), (S, M)
     S = bi.bi_gemm_splitk_for(N, K)
-    Xw = torch.zeros((16, K + 64), dtype=X.dtype, device="cuda")
-    Xw[:, 32:32 + K] = X[:16]
-    Yw = torch.zeros((16, N + 24), dtype=X.dtype, device="cuda")
-    bi.bi_gemm_splitk(Xw[:, 32:32 + K], Wt, y=Yw[:, 8:8 + N], split_k=S)
-    torch.cuda.synchronize()
-    assert np.array_equal(host_u16(Yw[:, 8:8 + N]), host_u16(bi.bi_gemm_splitk(X, Wt, split_k=S))[:16])
-    assert not Yw[:, :8].view(torch.int16).any() and not Yw[:, 8 + N:].view(torch.int16).any()
+    ref = host_u16(bi.bi_gemm_splitk(X, Wt, split_k=S))
+    for M in (5, 16, 29):
+        Xw = torch.zeros((M, K + 64), dtype=X.dtype, device="cuda")
+        Xw[:, 32:32 + K] = X[:M]
+        Yw = torch.zeros((M, N + 24), dtype=X.dtype, device="cuda")
+        bi.bi_gemm_splitk(Xw[:, 32:32 + K], Wt, y=Yw[:, 8:8 + N], split_k=S)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u16(Yw[:, 8:8 + N]), ref[:M]), M
+        assert not Yw[:, :8].view(torch.int16).any() and not Yw[:, 8 + N:].view(torch.int16).any()
 
 
 @pytest.mark.parametrize("shape_index", [0, 1, 2, 3])
