@@ -100,7 +100,7 @@ def test_splitk_partials_and_exact_combine(bi):
 
 @pytest.mark.parametrize("M,N,K,S", [(1, 1032, 4096, 32), (16, 1032, 4096, 4), (7, 264, 14336, 8), (5, 520, 3072, 8),
                                      (3, 4096, 2048, 16), (17, 1032, 4096, 32), (32, 264, 14336, 8),
-                                     (25, 520, 3072, 2)])
+                                     (25, 520, 3072, 2), (3, 264, 8192, 64), (16, 1032, 16384, 64)])
 def test_splitk_one_launch_partials_and_fold(bi, M, N, K, S):
     """Batches of at most 16 rows take the one-launch kernel (chunks folded in
     LDS), larger ones the partial and fold kernels.  Either way the workspace
