@@ -22,7 +22,8 @@ scaled to that clock (the published peak assumes 2.4 GHz).
 
 After the step, the rest of the headline metric is graph-timed on its own:
 ``gemm_over_m`` (bi_gemm at M = 2048, 4096, 8192 on the four projections, with
-geometric means), ``rmsnorm`` (GB/s over rotated copies, beside a plain device
+geometric means), ``gemm_fill_over_m`` (the same for bi_gemm_fill, whose bits
+equal bi_gemm's at every M but whose tile follows M), ``rmsnorm`` (GB/s over rotated copies, beside a plain device
 copy of the same bytes), ``shrink`` (the variants at M = 4096 and the two
 latency ratios the LoRA page reports), the shrink's replay variation, and
 ``stream70b`` (the Llama-3-70B MLP shape over a 200-batch dynamic stream).
@@ -286,11 +287,16 @@ def metric_parts(bi, torch, dev, H, Wq, Wkv, Wup, Wdown, A, G, eps):
     shapes = (("q", Wq), ("kv", Wkv), ("up", Wup), ("down", Wdown))
     g_out = {"kernel": "bi_gemm (one tile configuration per (N, K))", "peak_tflops": PEAK_BF16_TFLOPS,
              "shapes": {}}
-    fracs = []
+    # bi_gemm_fill: the same bits as bi_gemm at every M (each configuration
+    # runs the same matrix-core steps in the same order) with the tile picked
+    # from M; reported beside the single-configuration figures, not instead
+    f_out = {"kernel": "bi_gemm_fill (bi_gemm's bits; tile chosen per call from M)",
+             "peak_tflops": PEAK_BF16_TFLOPS, "shapes": {}}
+    fracs, ffracs = [], []
     for name, W in shapes:
         N, K = W.shape
         y = torch.empty((8192, N), dtype=torch.bfloat16, device=dev)
-        pts = {}
+        pts, fpts = {}, {}
         for M in (2048, 4096, 8192):
             xm, ym = xp[K][:M], y[:M]
             ms = _time_loop(torch, lambda i: bi.bi_gemm(xm, W, y=ym), 20)
@@ -298,14 +304,31 @@ def metric_parts(bi, torch, dev, H, Wq, Wkv, Wup, Wdown, A, G, eps):
             pts[str(M)] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1),
                            "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
             fracs.append(tf / PEAK_BF16_TFLOPS)
+            cf = bi.bi_gemm_fill_config_id(M, N, K)
+            if cf != bi.bi_gemm_config_id(N, K):
+                # gate: bi_gemm_fill is timed only if it reproduces bi_gemm's bits here
+                y2 = bi.bi_gemm_fill(xm, W)
+                if not torch.equal(y2.view(torch.int16), ym.view(torch.int16)):
+                    raise SystemExit(f"bi_gemm_fill differs from bi_gemm at M={M} N={N} K={K}")
+                del y2
+                ms = _time_loop(torch, lambda i: bi.bi_gemm_fill(xm, W, y=ym), 20)
+                tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            fpts[str(M)] = {"config": cf, "us": round(ms * 1e3, 2), "tflops": round(tf, 1),
+                            "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+            ffracs.append(tf / PEAK_BF16_TFLOPS)
         gm = _geomean([v["frac"] for v in pts.values()])
         g_out["shapes"][name] = {"K": K, "N": N, "config": bi.bi_gemm_config_id(N, K), "M": pts,
                                  "geomean_frac": round(gm, 4)}
-        print(f"# gemm over M {name}: " + ", ".join(f"M={m} {v['frac']:.3f}" for m, v in pts.items()),
+        f_out["shapes"][name] = {"K": K, "N": N, "M": fpts,
+                                 "geomean_frac": round(_geomean([v["frac"] for v in fpts.values()]), 4)}
+        print(f"# gemm over M {name}: " + ", ".join(f"M={m} {v['frac']:.3f}" for m, v in pts.items())
+              + "; fill: " + ", ".join(f"M={m} {v['frac']:.3f}" for m, v in fpts.items()),
               file=sys.stderr, flush=True)
         del y
     g_out["geomean_frac_all"] = round(_geomean(fracs), 4)
+    f_out["geomean_frac_all"] = round(_geomean(ffracs), 4)
     res["gemm_over_m"] = g_out
+    res["gemm_fill_over_m"] = f_out
     del xp
 
     # RMSNorm, K = 4096, inputs and outputs rotated over >= 1 GiB
