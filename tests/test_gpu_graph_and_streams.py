@@ -148,3 +148,50 @@ def test_graph_decode_step_follows_device_lengths(bi):
         if prev is not None:                     # the replay read the new lengths
             assert not torch.equal(prev[0].view(torch.int16), got_o[0].view(torch.int16)), rep
         prev = got_o
+
+
+def test_graph_replays_split_k_both_launch_forms(bi):
+    """The fixed split-K GEMM in a graph: a 4-row batch (one launch, chunks
+    folded in LDS) and a 40-row batch (partial kernel, then the fold), each
+    with its own workspace.  Every replay, with eager work between, gives the
+    eager bits and the eager partials."""
+    K, N = 4096, 1024
+    S = bi.bi_gemm_splitk_for(N, K)
+    W = dev_bf16(synth.normal_bf16((N, K), 9011, std=0.02))
+    cases = []
+    for M in (4, 40):
+        X = dev_bf16(synth.normal_bf16((M, K), 9012 + M))
+        ws_e = torch.zeros(bi.bi_gemm_splitk_workspace_bytes(M, N, S), dtype=torch.uint8, device="cuda")
+        y_e = bi.bi_gemm_splitk(X, W, split_k=S, ws=ws_e)
+        ws_g = torch.zeros_like(ws_e)
+        y_g = torch.empty_like(y_e)
+        cases.append((X, ws_e, y_e, ws_g, y_g))
+    torch.cuda.synchronize()
+
+    def run():
+        for X, _, _, ws_g, y_g in cases:
+            bi.bi_gemm_splitk(X, W, y=y_g, split_k=S, ws=ws_g)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()                                     # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        for _, _, _, ws_g, y_g in cases:
+            ws_g.zero_()
+            y_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"split-K graph replay {rep}")
+        for X, ws_e, y_e, ws_g, y_g in cases:
+            assert torch.equal(y_e.view(torch.int16), y_g.view(torch.int16)), (rep, X.shape[0])
+            assert torch.equal(ws_e, ws_g), (rep, X.shape[0])
+        for X, *_ in cases:                        # eager work between replays
+            bi.bi_gemm_splitk(X, W, split_k=S)
+        torch.cuda.synchronize()
