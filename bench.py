@@ -534,8 +534,10 @@ class ClockSampler:
             if not clks and self._num(m.get("current_gfxclk")):
                 clks = [self._num(m.get("current_gfxclk"))]
             power = self._num(m.get("current_socket_power")) or self._num(m.get("average_socket_power"))
+            # memory (UMC) clock, where the metrics table reports one
+            uclk = self._num(m.get("current_uclk")) or self._num(m.get("average_uclk_frequency"))
             if clks and time.time() - t0 >= self.skip:
-                r = (sum(clks) / len(clks), power)
+                r = (sum(clks) / len(clks), power, uclk)
                 if not self.samples or self.samples[-1] != r:
                     self.samples.append(r)
             self._stop.wait(self.period)
@@ -555,8 +557,9 @@ class ClockSampler:
         if not self.samples:
             return {"source": "amdsmi gpu_metrics", "readings": 0,
                     "error": self.err or f"no reading after the first {self.skip} s"}
-        mhz = [c for c, _ in self.samples]
-        watts = [w for _, w in self.samples if w]
+        mhz = [c for c, _, _ in self.samples]
+        watts = [w for _, w, _ in self.samples if w]
+        uclk = [u for _, _, u in self.samples if u]
         mean = sum(mhz) / len(mhz)
         peak_at_clock = PEAK_BF16_TFLOPS * mean / SPEC_SCLK_MHZ
         return {"source": "amdsmi gpu_metrics, sampled during the untimed settle steps",
@@ -564,6 +567,7 @@ class ClockSampler:
                 "sclk_mhz_min": round(min(mhz), 1), "sclk_mhz_max": round(max(mhz), 1),
                 "spec_sclk_mhz": SPEC_SCLK_MHZ,
                 "socket_power_w_mean": round(sum(watts) / len(watts), 1) if watts else None,
+                "mclk_mhz_mean": round(sum(uclk) / len(uclk), 1) if uclk else None,
                 "mfma_peak_at_mean_clock": round(peak_at_clock, 1),
                 "roofline_frac_at_mean_clock": round(achieved_tflops / peak_at_clock, 4)}
 

@@ -34,11 +34,12 @@ def test_recorded_traffic_tracks_the_gemm_code(tmp_path, monkeypatch):
 
 def test_clock_summary():
     c = bench.ClockSampler()
-    c.samples = [(1800.0, 1300.0), (1700.0, None), (1750.0, 1400.0)]
+    c.samples = [(1800.0, 1300.0, 1900.0), (1700.0, None, None), (1750.0, 1400.0, 1800.0)]
     s = c.summary(1300.0)
     assert s["readings"] == 3 and s["sclk_mhz_mean"] == 1750.0
     assert s["sclk_mhz_min"] == 1700.0 and s["sclk_mhz_max"] == 1800.0
     assert s["socket_power_w_mean"] == 1350.0
+    assert s["mclk_mhz_mean"] == 1850.0
     peak = bench.PEAK_BF16_TFLOPS * 1750.0 / bench.SPEC_SCLK_MHZ
     assert s["mfma_peak_at_mean_clock"] == round(peak, 1)
     assert s["roofline_frac_at_mean_clock"] == round(1300.0 / peak, 4)
