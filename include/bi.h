@@ -208,7 +208,8 @@ int bi_gemm_fill_config_id(int64_t M, int64_t N, int64_t K);
  * then bf16( (((p_0 + p_1) + p_2) + ...) + p_{S-1} ) in fp32, rounded to nearest
  * even once.  split_k == 1 gives bi_gemm's bits.
  * Launches: M <= 16 with K / split_k a multiple of 128 runs one kernel (each
- * workgroup owns 16 columns and every chunk, and folds in LDS); other sizes
+ * workgroup owns 16 columns, or 8 for narrow outputs, and every chunk, and
+ * folds in LDS); other sizes
  * run the partial kernel and then the fold.  Both write the same partials to
  * ws and return the same bits, so a row's result does not depend on which
  * one its batch took.
