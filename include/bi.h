@@ -251,7 +251,7 @@ int bi_gemm_splitk_noalloc(const uint16_t *x, const uint16_t *w, uint16_t *y,
                            int64_t ldx, int64_t ldw, int64_t ldy, int split_k, void *stream);
 
 /* bi_gemm_splitk_for -- a split factor for (N, K) that fills the chip at M <= 64
- * (a power of two, at least 4 K-stages per chunk), or -1 if (N, K) is not
+ * (a power of two, at least 8 32-k steps per chunk), or -1 if (N, K) is not
  * supported.  No M parameter, for the same reason as bi_gemm_config_id. */
 int bi_gemm_splitk_for(int64_t N, int64_t K);
 

@@ -261,7 +261,8 @@ def test_gemm_splitk_validation(lib):
     for N, K in ((4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336), (28672, 8192)):
         s = lib.bi_gemm_splitk_for(N, K)
         assert s >= 1 and (s & (s - 1)) == 0 and K % (32 * s) == 0
-    assert lib.bi_gemm_splitk_for(4096, 4096) == 8 and lib.bi_gemm_splitk_for(1024, 4096) == 32
+    assert [lib.bi_gemm_splitk_for(N, K) for N, K in ((4096, 4096), (1024, 4096), (14336, 4096),
+                                                      (4096, 14336), (28672, 8192))] == [8, 16, 4, 8, 2]
     h = lib.bi_gemm_splitk_noalloc
     assert h(X, None, Y, *a, 8, None) == BI_ERR_NULL
     assert h(X, W, Y, *a, 0, None) == BI_ERR_UNSUPPORTED

@@ -53,7 +53,7 @@ def _run_both(lib, X, Wt, M, N, K, S):
 
 def test_noalloc_equals_workspace_entry_point(lib):
     """Up projection (K = 4096, N = 14336, split 4) at M = 64, then KV
-    (N = 1024, split 32) at M = 5: bit for bit equal to bi_gemm_splitk, and the
+    (N = 1024, split 16) at M = 5: bit for bit equal to bi_gemm_splitk, and the
     sampled rows within tolerance of the oracle."""
     c = workloads.LLAMA8B
     x = workloads.llama8b_x(4096, rows=64)
