@@ -9,8 +9,8 @@ at Llama-3-8B projection shapes (K = 4096):
     D  = bi_gemm(U, Wdown)  K = 14336, N = 4096
     L  = bi_lora_shrink(H, A, split 8)   and the unsplit pass and the atomic
          control (A [16, 4096] ~ N(0, 0.01^2), fp32 out)
-    bi_row_bitdiff: probe rows of every output (H, Q, KV, U, D, L, Lu) against
-         the same rows computed alone, counted on every timed step
+    bi_row_bitdiff_batch: probe rows of every output (H, Q, KV, U, D, L, Lu) against
+         the same rows computed alone, in one launch, counted on every timed step
 Inputs are resident in HBM before timing starts.  ``value`` is the step's
 algorithmic TFLOP/s (2*M*N*K per GEMM, 2*M*R*K per shrink) over the timed
 steps.  ``roofline`` is for the dominant kernel (the 256x256-tile GEMM, which
@@ -172,9 +172,9 @@ def main():
         bi.bi_lora_shrink(H, A, y=Lu, split_k=1)
         bi.bi_lora_shrink_atomic(H, A, y=La, split_k=8)
         cs = counts[slot] if slot is not None else scratch_counts
-        for j, name in enumerate(outs):
-            bi.bi_row_bitdiff(outs[name], solo[name], probe_pos, probe_ids, counts=cs[j],
-                              check_rows=False)
+        # every output's probe rows against their solo rows, in one launch
+        bi.bi_row_bitdiff_batch([(outs[name], solo[name], probe_pos, probe_ids, cs[j])
+                                 for j, name in enumerate(outs)], check_rows=False)
 
     # Gate before timing: the path must be batch-invariant on this input.
     step(False, slot=0)

@@ -441,6 +441,39 @@ int bi_row_bitdiff(const void *a, int64_t lda, const int64_t *a_rows,
                    int64_t nrows, int64_t ncols, int elem_bytes,
                    uint64_t *counts, void *stream);
 
+/*
+ * bi_row_bitdiff_batch -- up to BI_BITDIFF_BATCH_MAX comparisons of
+ * bi_row_bitdiff in one launch (a step's outputs checked together).
+ *
+ * Defined by: the same passage as bi_row_bitdiff ("God Does Not Play Dice:
+ * Enforcing Batch Invariance in Agentic Kernel Generation", abstract).
+ *
+ *   items   HOST array of nitems descriptors (read during the call only); each
+ *           has bi_row_bitdiff's arguments and meaning, its counts written as
+ *           there.  1 <= nitems <= BI_BITDIFF_BATCH_MAX (else
+ *           BI_ERR_UNSUPPORTED).
+ * Every row must start 16-byte aligned and hold a whole number of 16-byte
+ * vectors (a, b 16-byte aligned; lda, ldb and ncols times elem_bytes
+ * multiples of 16), else BI_ERR_ALIGN.  Any invalid item rejects the whole
+ * call before anything is launched.  Same counts as one bi_row_bitdiff call
+ * per item.
+ */
+#define BI_BITDIFF_BATCH_MAX 16
+typedef struct bi_bitdiff_item {
+    const void *a;
+    int64_t lda;
+    const int64_t *a_rows;
+    const void *b;
+    int64_t ldb;
+    const int64_t *b_rows;
+    int64_t nrows;
+    int64_t ncols;
+    int64_t elem_bytes;
+    uint64_t *counts;
+} bi_bitdiff_item;
+
+int bi_row_bitdiff_batch(const bi_bitdiff_item *items, int nitems, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

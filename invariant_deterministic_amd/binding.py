@@ -73,12 +73,24 @@ _lib_shrink_atomic = _sig("bi_lora_shrink_atomic",
                           [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _int, _p])
 _lib_row_bitdiff = _sig("bi_row_bitdiff", [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _int, _p, _p])
 
+
+class BitdiffItem(ctypes.Structure):
+    """bi_bitdiff_item (include/bi.h): all fields 8 bytes wide."""
+    _fields_ = [("a", _p), ("lda", _i64), ("a_rows", _p), ("b", _p), ("ldb", _i64),
+                ("b_rows", _p), ("nrows", _i64), ("ncols", _i64), ("elem_bytes", _i64),
+                ("counts", _p)]
+
+
+BITDIFF_BATCH_MAX = 16   # BI_BITDIFF_BATCH_MAX
+_lib_row_bitdiff_batch = _sig("bi_row_bitdiff_batch", [ctypes.POINTER(BitdiffItem), _int, _p])
+
 BI_OK = 0
 EXPORTS = ("bi_abi_version", "bi_status_str", "bi_rmsnorm", "bi_gemm", "bi_gemm_config_id",
            "bi_gemm_num_configs", "bi_gemm_with_config", "bi_gemm_launch_plan", "bi_gemm_fill", "bi_gemm_fill_config_id",
            "bi_gemm_splitk",
            "bi_gemm_splitk_workspace_bytes", "bi_gemm_splitk_for", "bi_gemm_splitk_noalloc", "bi_gemm_mswitch_control", "bi_lora_shrink_workspace_bytes",
            "bi_lora_shrink", "bi_lora_shrink_two_pass", "bi_lora_shrink_atomic", "bi_row_bitdiff",
+           "bi_row_bitdiff_batch",
            "bi_decode_attention", "bi_decode_attention_workspace_bytes", "bi_lora_expand",
            "bi_lora_shrink_expand")
 
@@ -397,6 +409,48 @@ def bi_row_bitdiff(a: torch.Tensor, b: torch.Tensor, a_rows: torch.Tensor | None
                             nrows, ncols, a.element_size(), counts.data_ptr(), _stream(stream)),
            "bi_row_bitdiff")
     return counts
+
+
+def bi_row_bitdiff_batch(items, stream=None, check_rows: bool = True) -> list:
+    """Several bi_row_bitdiff comparisons in one launch.  ``items``: a sequence
+    of (a, b, a_rows, b_rows, counts) with the arguments of bi_row_bitdiff
+    (counts may be None).  Returns the counts tensors, one per item."""
+    items = list(items)
+    if not 1 <= len(items) <= BITDIFF_BATCH_MAX:
+        raise ValueError(f"1 to {BITDIFF_BATCH_MAX} items")
+    arr = (BitdiffItem * len(items))()
+    outs = []
+    for k, (a, b, a_rows, b_rows, counts) in enumerate(items):
+        if a.element_size() != b.element_size() or a.element_size() not in (2, 4):
+            raise TypeError("a and b need the same 2- or 4-byte element size")
+        ncols = a.shape[1]
+        if b.shape[1] != ncols:
+            raise ValueError("a and b disagree on the number of columns")
+        nrows = a_rows.numel() if a_rows is not None else (
+            b_rows.numel() if b_rows is not None else a.shape[0])
+        for rows, name, t in ((a_rows, "a_rows", a), (b_rows, "b_rows", b)):
+            if rows is None:
+                if nrows > t.shape[0]:
+                    raise IndexError("more rows compared than present")
+                continue
+            if rows.dtype != torch.int64 or not rows.is_cuda or rows.numel() != nrows:
+                raise ValueError(f"{name} must be a device int64 vector of {nrows} indices")
+            if check_rows and nrows and not (0 <= int(rows.min()) and int(rows.max()) < t.shape[0]):
+                raise IndexError(f"{name} out of range")
+        if counts is None:
+            counts = torch.empty((nrows, 2), dtype=torch.int64, device=a.device)
+        else:
+            _want(counts, (nrows, 2), "counts")
+            if counts.dtype != torch.int64 or not counts.is_contiguous():
+                raise ValueError("counts must be a contiguous int64 [nrows, 2] tensor")
+        pa, lda = _mat(a, "a", (a.dtype,))
+        pb, ldb = _mat(b, "b", (b.dtype,))
+        arr[k] = BitdiffItem(pa, lda, a_rows.data_ptr() if a_rows is not None else None, pb, ldb,
+                             b_rows.data_ptr() if b_rows is not None else None, nrows, ncols,
+                             a.element_size(), counts.data_ptr())
+        outs.append(counts)
+    _check(_lib_row_bitdiff_batch(arr, len(items), _stream(stream)), "bi_row_bitdiff_batch")
+    return outs
 
 
 def bi_decode_attention_workspace_bytes(B: int, H: int, Tmax: int, D: int, split_size: int) -> int:

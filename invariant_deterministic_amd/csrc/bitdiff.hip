@@ -90,10 +90,127 @@ __global__ __launch_bounds__(kThreads) void row_bitdiff_kernel(
   }
 }
 
+// Several comparisons in one launch: workgroup r takes row r - start[i] of
+// item i, where start[i] <= r < start[i + 1].  The same per-row count as
+// row_bitdiff_kernel (every row here takes the 16-byte path: the host
+// requires it).  The item table travels by value as a kernel argument.
+struct BatchArgs {
+  const void *a[BI_BITDIFF_BATCH_MAX];
+  const void *b[BI_BITDIFF_BATCH_MAX];
+  const int64_t *a_rows[BI_BITDIFF_BATCH_MAX];
+  const int64_t *b_rows[BI_BITDIFF_BATCH_MAX];
+  unsigned long long *counts[BI_BITDIFF_BATCH_MAX];
+  int64_t lda[BI_BITDIFF_BATCH_MAX], ldb[BI_BITDIFF_BATCH_MAX], ncols[BI_BITDIFF_BATCH_MAX];
+  int64_t start[BI_BITDIFF_BATCH_MAX + 1];
+  int elem_bytes[BI_BITDIFF_BATCH_MAX];
+  int n;
+};
+
+__global__ __launch_bounds__(kThreads) void row_bitdiff_batch_kernel(const BatchArgs args) {
+  const int64_t g = blockIdx.x;
+  int i = 0;
+  while (i + 1 < args.n && g >= args.start[i + 1]) ++i;  // uniform over the workgroup
+  const int64_t r = g - args.start[i];
+  const int64_t ra = args.a_rows[i] ? args.a_rows[i][r] : r;
+  const int64_t rb = args.b_rows[i] ? args.b_rows[i][r] : r;
+  const int eb = args.elem_bytes[i];
+  const u32x4 *va = reinterpret_cast<const u32x4 *>(static_cast<const char *>(args.a[i]) + ra * args.lda[i] * eb);
+  const u32x4 *vb = reinterpret_cast<const u32x4 *>(static_cast<const char *>(args.b[i]) + rb * args.ldb[i] * eb);
+  const int64_t nv = args.ncols[i] * eb / 16;
+  unsigned long long bits = 0, elems = 0;
+  constexpr int U = 4;
+  for (int64_t c0 = threadIdx.x; c0 < nv; c0 += (int64_t)kThreads * U) {
+    u32x4 xa[U], xb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + (int64_t)u * kThreads;
+      if (c < nv) {
+        xa[u] = va[c];
+        xb[u] = vb[c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + (int64_t)u * kThreads;
+      if (c < nv) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t d = xa[u][j] ^ xb[u][j];
+          bits += (unsigned long long)__popc(d);
+          if (eb == 4) {
+            elems += d ? 1ull : 0ull;
+          } else {
+            elems += (d & 0xFFFFu) ? 1ull : 0ull;
+            elems += (d >> 16) ? 1ull : 0ull;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    bits += __shfl_xor(bits, off, 64);
+    elems += __shfl_xor(elems, off, 64);
+  }
+  __shared__ unsigned long long sb[kThreads / 64], se[kThreads / 64];
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sb[wv] = bits;
+    se[wv] = elems;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long tb = 0, te = 0;
+    for (int k = 0; k < kThreads / 64; ++k) {
+      tb += sb[k];
+      te += se[k];
+    }
+    args.counts[i][2 * r] = tb;
+    args.counts[i][2 * r + 1] = te;
+  }
+}
+
 }  // namespace
 }  // namespace bi
 
 using namespace bi;
+
+extern "C" int bi_row_bitdiff_batch(const bi_bitdiff_item *items, int nitems, void *stream) {
+  if (!items) return BI_ERR_NULL;
+  if (nitems < 1 || nitems > BI_BITDIFF_BATCH_MAX) return BI_ERR_UNSUPPORTED;
+  BatchArgs args{};
+  args.n = nitems;
+  int64_t total = 0;
+  for (int i = 0; i < nitems; ++i) {
+    const bi_bitdiff_item &it = items[i];
+    if (!it.a || !it.b || !it.counts) return BI_ERR_NULL;
+    if (it.elem_bytes != 2 && it.elem_bytes != 4) return BI_ERR_UNSUPPORTED;
+    if (it.nrows < 0 || it.ncols <= 0 || it.lda < it.ncols || it.ldb < it.ncols ||
+        it.nrows > 0x7FFFFFFF)
+      return BI_ERR_SHAPE;
+    // every row must start 16-byte aligned and hold whole 16-byte vectors
+    if (((uintptr_t)it.a | (uintptr_t)it.b) % 16 || (it.lda * it.elem_bytes) % 16 ||
+        (it.ldb * it.elem_bytes) % 16 || (it.ncols * it.elem_bytes) % 16 || ((uintptr_t)it.counts & 7))
+      return BI_ERR_ALIGN;
+    args.a[i] = it.a;
+    args.b[i] = it.b;
+    args.a_rows[i] = it.a_rows;
+    args.b_rows[i] = it.b_rows;
+    args.counts[i] = reinterpret_cast<unsigned long long *>(it.counts);
+    args.lda[i] = it.lda;
+    args.ldb[i] = it.ldb;
+    args.ncols[i] = it.ncols;
+    args.elem_bytes[i] = it.elem_bytes;
+    args.start[i] = total;
+    total += it.nrows;
+  }
+  args.start[nitems] = total;
+  if (total > 0x7FFFFFFF) return BI_ERR_SHAPE;
+  if (total == 0) return BI_OK;
+  hipLaunchKernelGGL(row_bitdiff_batch_kernel, dim3((unsigned)total), dim3(kThreads), 0,
+                     (hipStream_t)stream, args);
+  return launch_status();
+}
 
 extern "C" int bi_row_bitdiff(const void *a, int64_t lda, const int64_t *a_rows, const void *b,
                               int64_t ldb, const int64_t *b_rows, int64_t nrows, int64_t ncols,

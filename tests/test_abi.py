@@ -313,6 +313,46 @@ def test_bitdiff_validation(lib):
     assert f(X, 8, None, Y, 8, None, 0, 8, 2, WS, None) == BI_OK
 
 
+class _Item(ctypes.Structure):
+    # bi_bitdiff_item as include/bi.h lays it out: ten 8-byte fields
+    _fields_ = [("a", ctypes.c_void_p), ("lda", ctypes.c_int64), ("a_rows", ctypes.c_void_p),
+                ("b", ctypes.c_void_p), ("ldb", ctypes.c_int64), ("b_rows", ctypes.c_void_p),
+                ("nrows", ctypes.c_int64), ("ncols", ctypes.c_int64), ("elem_bytes", ctypes.c_int64),
+                ("counts", ctypes.c_void_p)]
+
+
+def test_bitdiff_batch_validation(rawlib):
+    """Every rejected call is rejected before a launch; an all-empty batch
+    returns BI_OK without one."""
+    if _gpu_visible():
+        pytest.skip("validation with fake addresses runs only where no GPU is visible")
+    assert ctypes.sizeof(_Item) == 80
+    f = rawlib.bi_row_bitdiff_batch
+    f.argtypes = [ctypes.POINTER(_Item), ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+
+    def call(items, n=None):
+        arr = (_Item * max(1, len(items)))(*items)
+        r = f(arr, len(items) if n is None else n, None)
+        assert r != BI_ERR_HIP
+        return r
+
+    good = _Item(X, 64, None, Y, 64, None, 3, 64, 2, WS)
+    assert f(None, 1, None) == BI_ERR_NULL
+    assert call([good], n=0) == BI_ERR_UNSUPPORTED
+    assert call([good] * 17) == BI_ERR_UNSUPPORTED
+    assert call([good, _Item(None, 64, None, Y, 64, None, 3, 64, 2, WS)]) == BI_ERR_NULL
+    assert call([good, _Item(X, 64, None, Y, 64, None, 3, 64, 2, None)]) == BI_ERR_NULL
+    assert call([_Item(X, 64, None, Y, 64, None, 3, 64, 8, WS), good]) == BI_ERR_UNSUPPORTED
+    assert call([good, _Item(X, 32, None, Y, 64, None, 3, 64, 2, WS)]) == BI_ERR_SHAPE
+    assert call([good, _Item(X, 64, None, Y, 64, None, -1, 64, 2, WS)]) == BI_ERR_SHAPE
+    assert call([good, _Item(X + 8, 64, None, Y, 64, None, 3, 64, 2, WS)]) == BI_ERR_ALIGN
+    assert call([good, _Item(X, 68, None, Y, 68, None, 3, 68, 2, WS)]) == BI_ERR_ALIGN  # 136-byte rows
+    assert call([good, _Item(X, 64, None, Y, 64, None, 3, 64, 2, WS + 4)]) == BI_ERR_ALIGN
+    empty = _Item(X, 64, None, Y, 64, None, 0, 64, 4, WS)
+    assert call([empty, empty]) == BI_OK
+
+
 def test_decode_attention_validation(lib):
     f = lib.bi_decode_attention
     need = lib.bi_decode_attention_workspace_bytes(2, 32, 1000, 128, 256)

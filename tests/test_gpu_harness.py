@@ -58,6 +58,39 @@ def test_bitdiff_signed_zero_and_nan_payload(bi):
     assert tuple(c[0]) == oracle.bitdiff(a[0], b[0]) == (8, 8)
 
 
+def test_bitdiff_batch_equals_single_calls(bi):
+    """bi_row_bitdiff_batch over items of both element sizes, with and without
+    row index vectors, strided and contiguous: every item's counts equal the
+    oracle's, hence those of one bi_row_bitdiff call per item."""
+    g = synth.rng(71)
+    items, want = [], []
+    for k, (nbits, rows, cols, gather) in enumerate(((16, 9, 256, False), (32, 5, 64, True),
+                                                       (16, 40, 4096, True), (32, 1, 16, False),
+                                                       (16, 3, 8, False))):
+        dtype = np.uint16 if nbits == 16 else np.uint32
+        sdt = np.int16 if nbits == 16 else np.int32
+        a = g.integers(0, 1 << nbits, size=(rows, cols + 8), dtype=np.uint64).astype(dtype)
+        b = a.copy()
+        for i, kk in zip(g.integers(0, rows * (cols + 8), size=50), g.integers(0, nbits, size=50)):
+            b.reshape(-1)[i] ^= dtype(1 << int(kk))
+        A = torch.from_numpy(a.view(sdt)).cuda()[:, :cols]        # strided views (row stride cols + 8)
+        B = torch.from_numpy(b.view(sdt)).cuda()[:, :cols]
+        if gather:
+            ar = g.permutation(rows)[: max(1, rows // 2)].astype(np.int64)
+            br = ar[::-1].copy()
+            items.append((A, B, torch.from_numpy(ar).cuda(), torch.from_numpy(br).cuda(), None))
+            want.append([oracle.bitdiff(a[ar[i], :cols], b[br[i], :cols]) for i in range(len(ar))])
+        else:
+            items.append((A, B, None, None, None))
+            want.append([oracle.bitdiff(a[r, :cols], b[r, :cols]) for r in range(rows)])
+    outs = bi.bi_row_bitdiff_batch(items)
+    for k, (c, w) in enumerate(zip(outs, want)):
+        c = c.cpu().numpy()
+        assert [tuple(x) for x in c] == w, k
+        single = bi.bi_row_bitdiff(*items[k][:4]).cpu().numpy()
+        assert np.array_equal(c, single), k
+
+
 def test_llama70b_dynamic_batch_stream(bi):
     """200 batches, M ~ U{1..4096}; 8 fixed probe rows at random positions must
     equal their solo outputs bit for bit; sampled rows match the oracle."""
