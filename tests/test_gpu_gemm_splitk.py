@@ -165,6 +165,27 @@ def test_splitk_parity_small_m(bi, shape_index):
                    f"K={K} N={N} M={M}")
 
 
+def test_splitk_llama70b_shape(bi):
+    """The 70B MLP shape (K = 8192, N = 28672, split 2 from the (N, K) rule):
+    one-launch batches (M = 1, 16; two wavefronts per workgroup) against the
+    oracle on 512 sampled columns, and bitwise against the same rows of a
+    40-row batch (partial kernel + fold)."""
+    c = workloads.LLAMA70B
+    K, N = c["K"], c["N"]
+    S = bi.bi_gemm_splitk_for(N, K)
+    assert S == 2
+    x = workloads.llama70b_x_pool()[:40]
+    w = workloads.llama70b_w()
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    ref = host_u16(bi.bi_gemm_splitk(X, Wt, split_k=S))
+    cols = np.sort(synth.rng(309).choice(N, size=512, replace=False))
+    for M in (1, 16):
+        say(f"splitk 70b shape M={M}")
+        y = host_u16(bi.bi_gemm_splitk(X[:M], Wt, split_k=S))
+        assert np.array_equal(y, ref[:M]), M
+        check_bf16(y[:, cols], oracle.gemm(x[:M], w[cols].copy()), f"70b M={M}")
+
+
 def test_splitk_batch_invariance(bi):
     """The split is fixed by (N, K): rows agree bitwise alone and in batches up
     to M = 1000, prefix and permuted."""
