@@ -23,7 +23,8 @@ scaled to that clock (the published peak assumes 2.4 GHz).
 After the step, the rest of the headline metric is graph-timed on its own:
 ``gemm_over_m`` (bi_gemm at M = 2048, 4096, 8192 on the four projections, with
 geometric means), ``gemm_fill_over_m`` (the same for bi_gemm_fill, whose bits
-equal bi_gemm's at every M but whose tile follows M), ``rmsnorm`` (GB/s over rotated copies, beside a plain device
+equal bi_gemm's at every M but whose tile follows M), ``gemm_small_m`` (the
+fixed split-K GEMM at M = 1, 16, 64: time and HBM GB/s), ``rmsnorm`` (GB/s over rotated copies, beside a plain device
 copy of the same bytes), ``shrink`` (the variants at M = 4096 and the two
 latency ratios the LoRA page reports), the shrink's replay variation, and
 ``stream70b`` (the Llama-3-70B MLP shape over a 200-batch dynamic stream).
@@ -329,6 +330,40 @@ def metric_parts(bi, torch, dev, H, Wq, Wkv, Wup, Wdown, A, G, eps):
     f_out["geomean_frac_all"] = round(_geomean(ffracs), 4)
     res["gemm_over_m"] = g_out
     res["gemm_fill_over_m"] = f_out
+
+    # Decode-sized batches: the fixed split-K GEMM (split from (N, K); one
+    # launch up to 16 rows) on each projection, the weight rotated over
+    # >= 1 GiB of copies so that it streams from HBM.  HBM-bound: bytes =
+    # 2(MK + NK + MN).  Gated: the rows of a batch equal those rows computed
+    # in a 65-row batch (the two-launch path) bit for bit.
+    GiB = 1 << 30
+    s_out = {"kernel": "bi_gemm_splitk (split from (N, K))", "bytes": "2*(M*K + N*K + M*N)",
+             "peak_gbs": PEAK_HBM_GBS, "shapes": {}}
+    for name, W in shapes:
+        N, K = W.shape
+        S = bi.bi_gemm_splitk_for(N, K)
+        cw = max(1, min(64, -(-GiB // (2 * N * K))))
+        Ws = [W] + [W.clone() for _ in range(cw - 1)]
+        x65 = xp[K][:65]
+        ref = bi.bi_gemm_splitk(x65, W, split_k=S)
+        pts = {}
+        for M in (1, 16, 64):
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(bi.bi_gemm_splitk_workspace_bytes(M, N, S), dtype=torch.uint8, device=dev)
+            bi.bi_gemm_splitk(x65[:M], W, y=y, split_k=S, ws=ws)
+            if not torch.equal(y.view(torch.int16), ref[:M].view(torch.int16)):
+                raise SystemExit(f"bi_gemm_splitk rows differ between batch sizes M={M} N={N} K={K}")
+            xm = x65[:M]
+            ms = _time_loop(torch, lambda i: bi.bi_gemm_splitk(xm, Ws[i % cw], y=y, split_k=S, ws=ws),
+                            4 * cw)
+            by = 2.0 * (M * K + N * K + M * N)
+            pts[str(M)] = {"us": round(ms * 1e3, 2), "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+                           "frac": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        s_out["shapes"][name] = {"K": K, "N": N, "split_k": S, "M": pts}
+        print(f"# split-K {name} (S={S}): " + ", ".join(f"M={m} {v['us']} us {v['frac']:.3f}" for m, v in pts.items()),
+              file=sys.stderr, flush=True)
+        del Ws
+    res["gemm_small_m"] = s_out
     del xp
 
     # RMSNorm, K = 4096, inputs and outputs rotated over >= 1 GiB
