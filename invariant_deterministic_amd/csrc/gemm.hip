@@ -19,8 +19,9 @@
 // form runs the same kernels at a ~10 % higher shader clock for the same
 // power, 5-9 % more throughput at M >= 4096.
 //
-// Data path per workgroup (4 wavefronts, 2 x 2 over the tile; the 256 x 256
-// tile's 64-k kernel runs 8 wavefronts in two ping-pong groups instead):
+// Data path per workgroup (4 compute wavefronts, 2 x 2 over the tile; the
+// 64-k kernels add four wavefronts that only load, and at 256 x 256 run two
+// ping-pong groups of four compute wavefronts instead):
 //   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS
 //          --ds_read_b128--> VGPR fragments --MFMA--> fp32 accumulators
 //   epilogue: accumulators -> bf16 (round to nearest even) -> LDS -> whole
@@ -506,30 +507,110 @@ __device__ __forceinline__ void gemm_mainloop2(f32x4 (&acc)[BN / 32][BM / 32], c
   mfma_step<BN, BM>(acc, f1);
 }
 
-// One BN x BM output tile with 64-k stages, at rows m0.., columns n0...
-template <int BN, int BM>
-__device__ __forceinline__ void wide_tile(char *lds, const uint16_t *__restrict__ x,
-                                          const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
-                                          int M, int N, int K, int64_t ldx, int64_t ldw,
-                                          int64_t ldy, int m0, int n0) {
-  using C = Cfg2<BN, BM>;
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wn = wv >> 1, wm = wv & 1;
-  f32x4 acc[C::FN][C::FM];
-  gemm_mainloop2<BN, BM, false>(acc, lds, x, w, M, N, K / BK2, ldx, ldw, m0, n0, wv, lane, K);
-  barrier_no_fence();  // every wavefront is done reading the stages
-  store_tile<BN, BM>(acc, lds, y, M, N, ldy, m0, n0, wn, wm, wv, lane);
-}
-
-template <int BN, int BM>
-__global__ __launch_bounds__(kThreads, 1) void gemm_wide_kernel(
+// Role-split form of the 64-k scheme (activations in the ring of 3): eight
+// wavefronts, two per SIMD.  Wavefronts 0-3 compute the 2 x 2 sub-tiles with
+// the fragment reads and products of gemm_mainloop2, in the same order, so the
+// bits are the same; wavefronts 4-7 only issue the direct-to-LDS loads, in
+// gemm_mainloop2's order and with its waits.  The two sides pass the same
+// sequence of barriers: one at the start, one per stage boundary, one when the
+// last stage is read.  With the loads out of the compute wavefronts'
+// instruction stream, an LDS stage is refilled while the other SIMD wavefront
+// multiplies.
+//
+// WPE: wavefronts per SIMD the register allocation must allow.  At 128 x 128
+// (80 KiB of LDS) two workgroups share a CU when it is 4, i.e. at most 128
+// VGPRs; the larger tiles take 128 KiB of LDS, one workgroup per CU.
+template <int BN, int BM, int WPE>
+__global__ __launch_bounds__(2 * kThreads, WPE) void gemm_split_role_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
     int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+  using C = Cfg2<BN, BM>;
   __shared__ __attribute__((aligned(1024))) char lds[wide_lds_bytes<BN, BM, false>()];
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  wide_tile<BN, BM>(lds, x, w, y, M, N, K, ldx, ldw, ldy, tm * BM, tn * BN);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool loader = wave >= 4;
+  const int wv = wave & 3;
+  const int wn = wv >> 1, wm = wv & 1;
+  const int nkb = K / BK2;
+  LoadPlan2<BN> pw;
+  LoadPlan2<BM> px;
+  if (loader) {
+    pw.init(w, N, n0, N, ldw, K, wv, lane);
+    px.init(x, M, m0, M, ldx, K, wv, lane);
+  }
+  f32x4 acc[C::FN][C::FM];
+#pragma unroll
+  for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x4{};
+  // slots: weights in a ring of 2 (current, next), activations in a ring of 3
+  char *wa = lds, *wb = wa + C::W_BYTES;
+  char *xa = lds + 2 * C::W_BYTES, *xb = xa + C::X_BYTES, *xf = xb + C::X_BYTES;
+  if (loader) {
+    pw.issue(wa, 0, wv);
+    px.issue(xa, 0, wv);
+    if (nkb > 1) {
+      pw.issue(wb, BK2, wv);
+      px.issue(xb, BK2, wv);
+      wait_vmcnt<C::LW + C::LX>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_no_fence();
+    int kb = 0;
+    for (; kb + 2 < nkb; ++kb) {
+      const int k2 = (kb + 2) * BK2;
+      px.issue(xf, k2, wv);  // x's free slot held stage kb - 1
+      wait_vmcnt<C::LX>();   // stage kb + 1 has landed; x stage kb + 2 may fly
+      barrier_no_fence();    // ... and every compute wavefront is done with stage kb
+      pw.issue(wa, k2, wv);
+      char *t = wa; wa = wb; wb = t;
+      t = xa; xa = xb; xb = xf; xf = t;
+    }
+    if (kb + 1 < nkb) {
+      wait_vmcnt<0>();
+      barrier_no_fence();
+    }
+    barrier_no_fence();  // the last stage is read
+    return;
+  }
+  barrier_no_fence();
+  Frags<BN, BM> f0, f1;
+  read_frags2<BN, BM>(f0, wa, xa, 0, wn, wm, lane);
+  int kb = 0;
+  for (; kb + 2 < nkb; ++kb) {
+    read_frags2<BN, BM>(f1, wa, xa, 1, wn, wm, lane);
+    mfma_step<BN, BM>(acc, f0);
+    interleave_even<C::FN * C::FM, 0, C::FN + C::FM>();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt0();
+    barrier_no_fence();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags2<BN, BM>(f0, wb, xb, 0, wn, wm, lane);
+    mfma_step<BN, BM>(acc, f1);
+    interleave_even<C::FN * C::FM, 0, C::FN + C::FM>();
+    __builtin_amdgcn_sched_barrier(0);
+    char *t = wa; wa = wb; wb = t;
+    t = xa; xa = xb; xb = xf; xf = t;
+  }
+  if (kb + 1 < nkb) {
+    read_frags2<BN, BM>(f1, wa, xa, 1, wn, wm, lane);
+    mfma_step<BN, BM>(acc, f0);
+    wait_lgkmcnt0();
+    barrier_no_fence();
+    read_frags2<BN, BM>(f0, wb, xb, 0, wn, wm, lane);
+    mfma_step<BN, BM>(acc, f1);
+    wa = wb;
+    xa = xb;
+  }
+  read_frags2<BN, BM>(f1, wa, xa, 1, wn, wm, lane);
+  mfma_step<BN, BM>(acc, f0);
+  mfma_step<BN, BM>(acc, f1);
+  barrier_no_fence();  // the last stage is read
+  store_tile<BN, BM>(acc, lds, y, M, N, ldy, m0, n0, wn, wm, wv, lane);
 }
 
 template <int BN, int BM>
@@ -880,15 +961,17 @@ struct CfgEntry {
   int wide_threads;   // workgroup size of `wide`
 };
 
-// The 256 x 256 tile's 64-k kernel is the 8-wavefront ping-pong one.  The
-// 4-wavefront form measured 15-20 % slower: its 256 accumulators per
-// wavefront fill every AGPR, and the compiler then copies them between
-// register files inside the K loop.
+// Every 64-k kernel runs 8 wavefronts.  At 256 x 256 they are two ping-pong
+// groups of four (the 4-wavefront form measured 15-20 % slower: its 256
+// accumulators per wavefront fill every AGPR, and the compiler then copies
+// them between register files inside the K loop).  The smaller tiles split
+// the roles: four compute, four load (4-13 % faster than four wavefronts
+// doing both, 8-9 % at 256 x 128).
 const CfgEntry kConfigs[] = {
     {256, 256, gemm_kernel<256, 256>, gemm_pp_kernel<256, 256>, 512},
-    {256, 128, gemm_kernel<256, 128>, gemm_wide_kernel<256, 128>, kThreads},
-    {128, 128, gemm_kernel<128, 128>, gemm_wide_kernel<128, 128>, kThreads},
-    {128, 256, gemm_kernel<128, 256>, gemm_wide_kernel<128, 256>, kThreads},
+    {256, 128, gemm_kernel<256, 128>, gemm_split_role_kernel<256, 128, 1>, 2 * kThreads},
+    {128, 128, gemm_kernel<128, 128>, gemm_split_role_kernel<128, 128, 4>, 2 * kThreads},
+    {128, 256, gemm_kernel<128, 256>, gemm_split_role_kernel<128, 256, 1>, 2 * kThreads},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
