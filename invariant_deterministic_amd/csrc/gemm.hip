@@ -507,25 +507,34 @@ __device__ __forceinline__ void gemm_mainloop2(f32x4 (&acc)[BN / 32][BM / 32], c
   mfma_step<BN, BM>(acc, f1);
 }
 
-// Role-split form of the 64-k scheme (activations in the ring of 3): eight
-// wavefronts, two per SIMD.  Wavefronts 0-3 compute the 2 x 2 sub-tiles with
-// the fragment reads and products of gemm_mainloop2, in the same order, so the
-// bits are the same; wavefronts 4-7 only issue the direct-to-LDS loads, in
-// gemm_mainloop2's order and with its waits.  The two sides pass the same
-// sequence of barriers: one at the start, one per stage boundary, one when the
-// last stage is read.  With the loads out of the compute wavefronts'
-// instruction stream, an LDS stage is refilled while the other SIMD wavefront
-// multiplies.
+// Role-split form of the 64-k scheme: eight wavefronts, two per SIMD.
+// Wavefronts 0-3 compute the 2 x 2 sub-tiles with the fragment reads and
+// products of gemm_mainloop2, in the same order, so the bits are the same;
+// wavefronts 4-7 only issue the direct-to-LDS loads and wait for them.  The
+// two sides pass the same sequence of barriers: B(b) before stage b is read
+// (stage b has landed and stage b - 1 is read, so its slots are free), for
+// b = 0 .. nkb - 1, and one when the last stage is read.  With the loads out
+// of the compute wavefronts' instruction stream, an LDS stage is refilled
+// while the other SIMD wavefront multiplies.
 //
-// WPE: wavefronts per SIMD the register allocation must allow.  At 128 x 128
-// (80 KiB of LDS) two workgroups share a CU when it is 4, i.e. at most 128
-// VGPRs; the larger tiles take 128 KiB of LDS, one workgroup per CU.
-template <int BN, int BM, int WPE>
+// Activations sit in a ring of 3 stages, weights in a ring of DW (2 or 3).
+// Stage s of an operand with a ring of D goes into slot s % D as soon as
+// stage s - D is read (after B(s - D + 1); stages 0 .. D - 1 before B(0)):
+// the weights run DW - 1 stages ahead, the activations two.
+// WPE: wavefronts per SIMD the register allocation must allow (4: at most
+// 128 VGPRs, so that two 80 KiB workgroups share a CU).
+template <int BN, int BM, int WPE, int DW>
 __global__ __launch_bounds__(2 * kThreads, WPE) void gemm_split_role_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
     int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
   using C = Cfg2<BN, BM>;
-  __shared__ __attribute__((aligned(1024))) char lds[wide_lds_bytes<BN, BM, false>()];
+  constexpr int DX = 3;
+  static_assert(DW == 2 || DW == 3, "weight ring");
+  // loads that may still fly when stage b >= 1 has landed: those issued after
+  // the later of W(b) and X(b), up to B(b) -- X(b + 1) when DW = 2, all of
+  // stage b + 1 when DW = 3
+  constexpr int WAITC = DW < DX ? C::LX : C::LW + C::LX;
+  __shared__ __attribute__((aligned(1024))) char lds[DW * C::W_BYTES + DX * C::X_BYTES];
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -535,6 +544,7 @@ __global__ __launch_bounds__(2 * kThreads, WPE) void gemm_split_role_kernel(
   const int wv = wave & 3;
   const int wn = wv >> 1, wm = wv & 1;
   const int nkb = K / BK2;
+  char *const xbase = lds + DW * C::W_BYTES;
   LoadPlan2<BN> pw;
   LoadPlan2<BM> px;
   if (loader) {
@@ -546,38 +556,45 @@ __global__ __launch_bounds__(2 * kThreads, WPE) void gemm_split_role_kernel(
   for (int i = 0; i < C::FN; ++i)
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x4{};
-  // slots: weights in a ring of 2 (current, next), activations in a ring of 3
-  char *wa = lds, *wb = wa + C::W_BYTES;
-  char *xa = lds + 2 * C::W_BYTES, *xb = xa + C::X_BYTES, *xf = xb + C::X_BYTES;
   if (loader) {
-    pw.issue(wa, 0, wv);
-    px.issue(xa, 0, wv);
-    if (nkb > 1) {
-      pw.issue(wb, BK2, wv);
-      px.issue(xb, BK2, wv);
-      wait_vmcnt<C::LW + C::LX>();
-    } else {
-      wait_vmcnt<0>();
+    int sw = 0, sx = 0;  // slots of the next weight and activation stages
+    auto issue_w = [&](int s) {
+      pw.issue(lds + sw * C::W_BYTES, s * BK2, wv);
+      sw = sw + 1 == DW ? 0 : sw + 1;
+    };
+    auto issue_x = [&](int s) {
+      px.issue(xbase + sx * C::X_BYTES, s * BK2, wv);
+      sx = sx + 1 == DX ? 0 : sx + 1;
+    };
+    // every slot starts free: stages 0 .. D - 1 of each operand, in stage order
+#pragma unroll
+    for (int s = 0; s < DX; ++s) {
+      if (s < DW && s < nkb) issue_w(s);
+      if (s < nkb) issue_x(s);
     }
-    barrier_no_fence();
-    int kb = 0;
-    for (; kb + 2 < nkb; ++kb) {
-      const int k2 = (kb + 2) * BK2;
-      px.issue(xf, k2, wv);  // x's free slot held stage kb - 1
-      wait_vmcnt<C::LX>();   // stage kb + 1 has landed; x stage kb + 2 may fly
-      barrier_no_fence();    // ... and every compute wavefront is done with stage kb
-      pw.issue(wa, k2, wv);
-      char *t = wa; wa = wb; wb = t;
-      t = xa; xa = xb; xb = xf; xf = t;
+    if (nkb >= DX) wait_vmcnt<(DW - 1) * C::LW + (DX - 1) * C::LX>();  // stage 0 has landed
+    else wait_vmcnt<0>();
+    barrier_no_fence();  // B(0)
+    int b = 1;
+    for (; b + DX - 1 < nkb; ++b) {
+      wait_vmcnt<WAITC>();  // stage b has landed
+      barrier_no_fence();   // B(b): stage b - 1 is read
+      issue_w(b + DW - 1);
+      issue_x(b + DX - 1);
     }
-    if (kb + 1 < nkb) {
-      wait_vmcnt<0>();
+    for (; b < nkb; ++b) {
+      if (b + DX - 2 < nkb) wait_vmcnt<WAITC>();
+      else wait_vmcnt<0>();
       barrier_no_fence();
+      if (b + DW - 1 < nkb) issue_w(b + DW - 1);
     }
     barrier_no_fence();  // the last stage is read
     return;
   }
-  barrier_no_fence();
+  // slots of stage b (a) and b + 1 (b), and the ring's third slot (c)
+  char *wa = lds, *wb = wa + C::W_BYTES, *wc = DW == 3 ? wb + C::W_BYTES : wa;
+  char *xa = xbase, *xb = xa + C::X_BYTES, *xc = xb + C::X_BYTES;
+  barrier_no_fence();  // B(0)
   Frags<BN, BM> f0, f1;
   read_frags2<BN, BM>(f0, wa, xa, 0, wn, wm, lane);
   int kb = 0;
@@ -587,14 +604,16 @@ __global__ __launch_bounds__(2 * kThreads, WPE) void gemm_split_role_kernel(
     interleave_even<C::FN * C::FM, 0, C::FN + C::FM>();
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt0();
-    barrier_no_fence();
+    barrier_no_fence();  // B(kb + 1)
     __builtin_amdgcn_sched_barrier(0);
     read_frags2<BN, BM>(f0, wb, xb, 0, wn, wm, lane);
     mfma_step<BN, BM>(acc, f1);
     interleave_even<C::FN * C::FM, 0, C::FN + C::FM>();
     __builtin_amdgcn_sched_barrier(0);
-    char *t = wa; wa = wb; wb = t;
-    t = xa; xa = xb; xb = xf; xf = t;
+    char *t = wa; wa = wb;
+    if constexpr (DW == 3) { wb = wc; wc = t; }
+    else wb = t;
+    t = xa; xa = xb; xb = xc; xc = t;
   }
   if (kb + 1 < nkb) {
     read_frags2<BN, BM>(f1, wa, xa, 1, wn, wm, lane);
@@ -966,12 +985,14 @@ struct CfgEntry {
 // accumulators per wavefront fill every AGPR, and the compiler then copies
 // them between register files inside the K loop).  The smaller tiles split
 // the roles: four compute, four load (4-13 % faster than four wavefronts
-// doing both, 8-9 % at 256 x 128).
+// doing both, 8-9 % at 256 x 128).  At 128 x 128 the weights take a ring of 3
+// too (96 KiB, one workgroup per CU): 11-20 % faster at M <= 4096 than the
+// ring of 2 with two workgroups per CU, 8 % slower at M = 8192.
 const CfgEntry kConfigs[] = {
     {256, 256, gemm_kernel<256, 256>, gemm_pp_kernel<256, 256>, 512},
-    {256, 128, gemm_kernel<256, 128>, gemm_split_role_kernel<256, 128, 1>, 2 * kThreads},
-    {128, 128, gemm_kernel<128, 128>, gemm_split_role_kernel<128, 128, 4>, 2 * kThreads},
-    {128, 256, gemm_kernel<128, 256>, gemm_split_role_kernel<128, 256, 1>, 2 * kThreads},
+    {256, 128, gemm_kernel<256, 128>, gemm_split_role_kernel<256, 128, 1, 2>, 2 * kThreads},
+    {128, 128, gemm_kernel<128, 128>, gemm_split_role_kernel<128, 128, 1, 3>, 2 * kThreads},
+    {128, 256, gemm_kernel<128, 256>, gemm_split_role_kernel<128, 256, 1, 2>, 2 * kThreads},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
