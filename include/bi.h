@@ -154,7 +154,11 @@ int bi_gemm_launch_plan(int64_t M, int64_t N, int64_t K, int64_t *plan);
  * (0 <= config < bi_gemm_num_configs()) instead of bi_gemm_config_id(N, K).
  * Every configuration runs the same reduction order, so all of them return the
  * same bits; this entry point exists to demonstrate exactly that and to time
- * the alternatives.  Same arguments and errors as bi_gemm, plus
+ * the alternatives.  Configurations 0-3 are single tiles (256 x 256,
+ * 256 x 128, 128 x 128, 128 x 256 outputs of w rows x x rows per workgroup);
+ * the last one is a mixed launch of 256 x 256 tiles whose last wave on each
+ * XCD, when it is at most half full, runs as 256 x 128 halves (with K % 64 ==
+ * 32 it runs as configuration 0).  Same arguments and errors as bi_gemm, plus
  * BI_ERR_UNSUPPORTED for an unknown config.
  */
 int bi_gemm_num_configs(void);
@@ -173,9 +177,10 @@ int bi_gemm_with_config(int config, const uint16_t *x, const uint16_t *w, uint16
  * the same matrix-core instruction over the same ascending k steps (see
  * bi_gemm_with_config), so the configuration can follow M without any output
  * bit following it: row i is still bitwise identical alone or in any batch.
- * The tile is the one with the smallest estimated time: waves of tiles over
- * the compute units times a measured per-tile cost.  bi_gemm keeps the single
- * (N, K)-keyed configuration.
+ * The configuration is the one with the smallest estimated time: waves of
+ * tiles over the compute units times a measured per-tile cost (for the mixed
+ * launch, each XCD's full waves plus one wave of half tiles).  bi_gemm keeps
+ * the single (N, K)-keyed configuration.
  *
  * Arguments, layout, ownership and errors as bi_gemm.
  */

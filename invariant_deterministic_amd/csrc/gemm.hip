@@ -523,21 +523,25 @@ __device__ __forceinline__ void gemm_mainloop2(f32x4 (&acc)[BN / 32][BM / 32], c
 // the weights run DW - 1 stages ahead, the activations two.
 // WPE: wavefronts per SIMD the register allocation must allow (4: at most
 // 128 VGPRs, so that two 80 KiB workgroups share a CU).
-template <int BN, int BM, int WPE, int DW>
-__global__ __launch_bounds__(2 * kThreads, WPE) void gemm_split_role_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
-    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+template <int BN, int BM, int DW>
+constexpr int role_lds_bytes() {
+  return DW * BN * kRow2 + 3 * BM * kRow2;
+}
+
+// Tile (tm, tn): rows tm * BM.., columns tn * BN.., by a workgroup of 512 threads.
+template <int BN, int BM, int DW>
+__device__ __forceinline__ void role_tile(char *lds, const uint16_t *__restrict__ x,
+                                          const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+                                          int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy,
+                                          int tm, int tn) {
   using C = Cfg2<BN, BM>;
+  const int m0 = tm * BM, n0 = tn * BN;
   constexpr int DX = 3;
   static_assert(DW == 2 || DW == 3, "weight ring");
   // loads that may still fly when stage b >= 1 has landed: those issued after
   // the later of W(b) and X(b), up to B(b) -- X(b + 1) when DW = 2, all of
   // stage b + 1 when DW = 3
   constexpr int WAITC = DW < DX ? C::LX : C::LW + C::LX;
-  __shared__ __attribute__((aligned(1024))) char lds[DW * C::W_BYTES + DX * C::X_BYTES];
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool loader = wave >= 4;
@@ -630,6 +634,16 @@ __global__ __launch_bounds__(2 * kThreads, WPE) void gemm_split_role_kernel(
   mfma_step<BN, BM>(acc, f1);
   barrier_no_fence();  // the last stage is read
   store_tile<BN, BM>(acc, lds, y, M, N, ldy, m0, n0, wn, wm, wv, lane);
+}
+
+template <int BN, int BM, int WPE, int DW>
+__global__ __launch_bounds__(2 * kThreads, WPE) void gemm_split_role_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char lds[role_lds_bytes<BN, BM, DW>()];
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  role_tile<BN, BM, DW>(lds, x, w, y, M, N, K, ldx, ldw, ldy, tm, tn);
 }
 
 template <int BN, int BM>
@@ -877,18 +891,22 @@ __global__ __launch_bounds__(64 * kFusedMaxWaves) void gemm_splitk_fused_kernel(
 //   group 1 issues weight stage j+2 while reading stage j (slot of j-1) and
 //   waits for stage j+1 before B(2j+2).
 template <int BN, int BM>
-__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
-    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+constexpr int pp_lds_bytes() {
+  return 2 * BM * kRow2 + 3 * BN * kRow2;
+}
+
+// Tile (tm, tn): rows tm * BM.., columns tn * BN.., by a workgroup of 512 threads.
+template <int BN, int BM>
+__device__ __forceinline__ void pp_tile(char *lds, const uint16_t *__restrict__ x,
+                                        const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+                                        int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy,
+                                        int tm, int tn) {
+  const int m0 = tm * BM, n0 = tn * BN;
   constexpr int QN = BN / 2, QM = BM / 2, WM = QM / 2;
   constexpr int FN = QN / 16, FM = WM / 16;  // 16x16 blocks per wave
   constexpr int WB = BN * kRow2, XB = BM * kRow2;
   constexpr int LW = BN / 32, LX = BM / 32;
-  static_assert(2 * XB + 3 * WB <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) char lds[2 * XB + 3 * WB];
-  int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  static_assert(pp_lds_bytes<BN, BM>() <= 160 * 1024, "LDS");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = wave & 3, g = wave >> 2;
@@ -971,6 +989,63 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
   store_sub<FN, FM>(acc, lds + wave * (WM * QN * 2), y, M, N, ldy, m0 + mw, n0 + nw, lane);
 }
 
+template <int BN, int BM>
+__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char lds[pp_lds_bytes<BN, BM>()];
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  pp_tile<BN, BM>(lds, x, w, y, M, N, K, ldx, ldw, ldy, tm, tn);
+}
+
+// 256 x 256 tiles with the last, at most half full wave of each XCD cut in
+// two.  The workgroups of XCD x (launch index % 8) take that XCD's range of
+// logical tiles as tile_of does; its full waves run as 256 x 256 tiles
+// (pp_tile), and when its remaining tiles would leave at least half of its
+// CUs idle, each of them runs as two 256 x 128 tiles (role_tile), which fill
+// the XCD.  Each output element still receives the same 32-k steps in
+// ascending order from one wavefront, so the bits equal every other
+// configuration's; only the number of outputs a workgroup owns changes.
+constexpr int kCusPerXcd = 32;  // MI355X: 256 CUs in 8 XCDs
+// Of c tiles on one XCD, how many run as halves.
+__host__ __device__ inline int mixed_tail(int c) {
+  const int t = c % kCusPerXcd;
+  return t <= kCusPerXcd / 2 ? t : 0;
+}
+// Workgroups per XCD slot of the launch (the launch has 8 times as many).
+__host__ __device__ inline int mixed_slots(int T) {
+  const int q = T >> 3, r = T & 7;
+  const int c0 = q + (r > 0 ? 1 : 0), c1 = q;  // tiles of XCD 0 and of XCD 7
+  const int n0 = c0 + mixed_tail(c0), n1 = c1 + mixed_tail(c1);
+  return n0 > n1 ? n0 : n1;
+}
+
+__global__ __launch_bounds__(512, 1) void gemm_mixed_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+  constexpr int PP = pp_lds_bytes<256, 256>(), RS = role_lds_bytes<256, 128, 2>();
+  __shared__ __attribute__((aligned(1024))) char lds[PP > RS ? PP : RS];
+  const int T = tiles_m * tiles_n;
+  const int q = T >> 3, r = T & 7;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int c = q + (xcd < r ? 1 : 0);
+  const int first = xcd * q + (xcd < r ? xcd : r);  // the XCD's first logical tile, as xcd_lid
+  const int tail = mixed_tail(c), full = c - tail;
+  int tm, tn;
+  if (local < full) {
+    group_tile(first + local, tiles_m, tiles_n, tm, tn);
+    pp_tile<256, 256>(lds, x, w, y, M, N, K, ldx, ldw, ldy, tm, tn);
+    return;
+  }
+  const int h = local - full;
+  if (h >= 2 * tail) return;  // slots past this XCD's share
+  group_tile(first + full + (h >> 1), tiles_m, tiles_n, tm, tn);
+  const int th = 2 * tm + (h & 1);  // the half as a 256 x 128 tile row
+  if (th * 128 >= M) return;        // a half wholly past the last row
+  role_tile<256, 128, 2>(lds, x, w, y, M, N, K, ldx, ldw, ldy, th, tn);
+}
+
 typedef void (*GemmKernel)(const uint16_t *, const uint16_t *, uint16_t *, int, int, int, int64_t,
                            int64_t, int64_t, int, int);
 struct CfgEntry {
@@ -978,6 +1053,7 @@ struct CfgEntry {
   GemmKernel kernel;  // BK = 32 stages, any K % 32 == 0 (256 threads)
   GemmKernel wide;    // BK = 64 stages, used when K % 64 == 0 (same k order, same bits)
   int wide_threads;   // workgroup size of `wide`
+  bool mixed;         // `wide` is gemm_mixed_kernel: its own workgroup count
 };
 
 // Every 64-k kernel runs 8 wavefronts.  At 256 x 256 they are two ping-pong
@@ -988,11 +1064,15 @@ struct CfgEntry {
 // doing both, 8-9 % at 256 x 128).  At 128 x 128 the weights take a ring of 3
 // too (96 KiB, one workgroup per CU): 11-20 % faster at M <= 4096 than the
 // ring of 2 with two workgroups per CU, 8 % slower at M = 8192.
+// The last configuration is the mixed 256 x 256 / 256 x 128 launch: only
+// bi_gemm_fill picks it (the split follows M), and with K % 64 == 32 it runs
+// as configuration 0.
 const CfgEntry kConfigs[] = {
-    {256, 256, gemm_kernel<256, 256>, gemm_pp_kernel<256, 256>, 512},
-    {256, 128, gemm_kernel<256, 128>, gemm_split_role_kernel<256, 128, 1, 2>, 2 * kThreads},
-    {128, 128, gemm_kernel<128, 128>, gemm_split_role_kernel<128, 128, 1, 3>, 2 * kThreads},
-    {128, 256, gemm_kernel<128, 256>, gemm_split_role_kernel<128, 256, 1, 2>, 2 * kThreads},
+    {256, 256, gemm_kernel<256, 256>, gemm_pp_kernel<256, 256>, 512, false},
+    {256, 128, gemm_kernel<256, 128>, gemm_split_role_kernel<256, 128, 1, 2>, 2 * kThreads, false},
+    {128, 128, gemm_kernel<128, 128>, gemm_split_role_kernel<128, 128, 1, 3>, 2 * kThreads, false},
+    {128, 256, gemm_kernel<128, 256>, gemm_split_role_kernel<128, 256, 1, 2>, 2 * kThreads, false},
+    {256, 256, gemm_kernel<256, 256>, gemm_mixed_kernel, 512, true},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1021,17 +1101,30 @@ int config_for(int64_t N, int64_t K) {
 // costs are measured ones, relative to 256 x 256: a 256 x 128 tile takes
 // ~0.68 of it, a 128 x 256 tile ~0.67, a 128 x 128 tile ~0.34 (so three
 // waves of either half-size tile do not replace two of the big tile, which
-// measured 1-9 % slower).  Ties keep the larger tile.
+// measured 1-9 % slower).  The mixed launch costs each XCD its full waves of
+// 256 x 256 tiles plus, if it cuts a tail, one wave of 256 x 128 tiles; it is
+// taken only for 64-k stages on a chip of 8 x kCusPerXcd CUs.  Ties keep the
+// earlier configuration.
 int fill_config_for(int64_t M, int64_t N, int64_t K) {
-  (void)K;
-  static const double kTileCost[kNumConfigs] = {1.0, 0.68, 0.34, 0.67};
+  static const double kTileCost[kNumConfigs] = {1.0, 0.68, 0.34, 0.67, 1.0};
   const int64_t cus = cu_count();
   int best = 0;
   double best_t = 0.0;
   for (int c = 0; c < kNumConfigs; ++c) {
     const int64_t tiles = ((M + kConfigs[c].bm - 1) / kConfigs[c].bm) *
                           ((N + kConfigs[c].bn - 1) / kConfigs[c].bn);
-    const double t = (double)((tiles + cus - 1) / cus) * kTileCost[c];
+    double t = (double)((tiles + cus - 1) / cus) * kTileCost[c];
+    if (kConfigs[c].mixed) {
+      if (K % BK2 || cus != 8 * kCusPerXcd || tiles > 0x7FFFFFFF) continue;
+      const int64_t q = tiles >> 3, r = tiles & 7;
+      t = 0.0;
+      for (int64_t cx : {q + (r > 0 ? 1 : 0), q}) {
+        const int tail = mixed_tail((int)cx);
+        const double tx = (double)((cx - tail + kCusPerXcd - 1) / kCusPerXcd) * kTileCost[c] +
+                          (tail ? kTileCost[1] : 0.0);
+        t = tx > t ? tx : t;
+      }
+    }
     if (c == 0 || t < best_t - 1e-9) {
       best = c;
       best_t = t;
@@ -1060,24 +1153,27 @@ int validate(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64
 
 // Everything a launch of configuration cfg depends on.  M enters only the
 // number of tile rows (how many workgroups run), never the kernel, its tile or
-// its K stage.
+// its K stage -- except in the mixed configuration, which bi_gemm never uses.
 struct Plan {
   int cfg, bm, bn, kstage, threads;
-  int64_t tiles_m, tiles_n;
+  int64_t tiles_m, tiles_n, groups;
   GemmKernel kern;
 };
 Plan plan_for(int cfg, int64_t M, int64_t N, int64_t K) {
   const CfgEntry &c = kConfigs[cfg];
   const bool wide = c.wide && K % BK2 == 0;
-  return Plan{cfg, c.bm, c.bn, wide ? BK2 : BK, wide ? c.wide_threads : kThreads,
-              (M + c.bm - 1) / c.bm, (N + c.bn - 1) / c.bn, wide ? c.wide : c.kernel};
+  const int64_t tm = (M + c.bm - 1) / c.bm, tn = (N + c.bn - 1) / c.bn;
+  int64_t groups = tm * tn;
+  if (wide && c.mixed && groups <= 0x7FFFFFFF) groups = 8 * (int64_t)mixed_slots((int)groups);
+  return Plan{cfg, c.bm, c.bn, wide ? BK2 : BK, wide ? c.wide_threads : kThreads, tm, tn, groups,
+              wide ? c.wide : c.kernel};
 }
 
 int launch(int cfg, const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, int64_t N,
            int64_t K, int64_t ldx, int64_t ldw, int64_t ldy, void *stream) {
   const Plan p = plan_for(cfg, M, N, K);
-  if (p.tiles_m * p.tiles_n > 0x7FFFFFFF) return BI_ERR_SHAPE;
-  hipLaunchKernelGGL(p.kern, dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(p.threads), 0,
+  if (p.tiles_m * p.tiles_n > 0x7FFFFFFF || p.groups > 0x7FFFFFFF) return BI_ERR_SHAPE;
+  hipLaunchKernelGGL(p.kern, dim3((unsigned)p.groups), dim3(p.threads), 0,
                      (hipStream_t)stream, x, w, y, (int)M, (int)N, (int)K, ldx, ldw, ldy,
                      (int)p.tiles_m, (int)p.tiles_n);
   return launch_status();
@@ -1107,9 +1203,9 @@ extern "C" int bi_gemm_launch_plan(int64_t M, int64_t N, int64_t K, int64_t *pla
   // the same function bi_gemm's launch() builds its launch from
   const Plan p = plan_for(cfg, M, N, K);
   int64_t kid = -1;
-  for (int c = 0; c < kNumConfigs; ++c) {
+  for (int c = 0; c < kNumConfigs && kid < 0; ++c) {  // the first entry holding the kernel
     if (p.kern == kConfigs[c].kernel) kid = 2 * c;
-    if (p.kern == kConfigs[c].wide) kid = 2 * c + 1;
+    else if (p.kern == kConfigs[c].wide) kid = 2 * c + 1;
   }
   plan[0] = p.cfg;
   plan[1] = kid;
@@ -1117,7 +1213,7 @@ extern "C" int bi_gemm_launch_plan(int64_t M, int64_t N, int64_t K, int64_t *pla
   plan[3] = p.bn;
   plan[4] = p.kstage;
   plan[5] = p.threads;
-  plan[6] = M == 0 ? 0 : p.tiles_m * p.tiles_n;
+  plan[6] = M == 0 ? 0 : p.groups;
   return BI_OK;
 }
 

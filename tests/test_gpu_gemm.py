@@ -234,6 +234,25 @@ def test_gemm_fill_same_bits_as_bi_gemm(bi):
         assert r["rows"] > 20 and r["diff_bits"] == 0, r
 
 
+@pytest.mark.parametrize("M,N", [(4096, 14336), (4200, 4096), (2305, 14336), (6144, 4096)])
+def test_gemm_mixed_launch(bi, M, N):
+    """The mixed launch (the last configuration) runs each XCD's full waves of
+    256 x 256 tiles and cuts a tail of at most half a wave into 256 x 128
+    halves; at M = 4200 and 2305 the last tile row is ragged, so some halves
+    lie wholly past M and store nothing.  Its bits equal configuration 0's,
+    and sampled columns match the oracle."""
+    K = 256
+    mixed = bi.bi_gemm_num_configs() - 1
+    x = synth.normal_bf16((M, K), 411 + M)
+    w = synth.normal_bf16((N, K), 412 + N, std=0.02)
+    X, Wt = dev_bf16(x), dev_bf16(w)
+    say(f"gemm mixed launch M={M} N={N} K={K}")
+    y = host_u16(bi.bi_gemm_with_config(mixed, X, Wt))
+    assert np.array_equal(y, host_u16(bi.bi_gemm_with_config(0, X, Wt)))
+    cols = np.sort(np.random.default_rng(M + N).choice(N, 48, replace=False))
+    check_bf16(y[:, cols], oracle.gemm(x, w[cols]), f"mixed M={M} N={N}")
+
+
 def test_gemm_runs_one_config_at_every_m(bi):
     """bi_gemm's output equals that of its own configuration
     (bi_gemm_config_id(N, K), reported by bi_gemm_launch_plan) at every M: the
