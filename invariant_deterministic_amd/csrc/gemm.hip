@@ -1277,12 +1277,17 @@ int splitk_launch(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, 
   hipStream_t s = (hipStream_t)stream;
   const int kc = (int)(K / split_k);
   if (M <= kFusedMaxM && kc % kFusedGroupK == 0) {
-    const int nw = split_k < kFusedMaxWaves ? split_k : kFusedMaxWaves;
     // 8-column workgroups when 16-column ones would leave at least half of the
     // CUs idle (every workgroup also fetches the activations, so splitting
     // further costs more than it gains: at N = 4096 8-column workgroups
     // measured 15-26 % slower, at N = 1024 3-7 % faster)
     const bool cols8 = 2 * ((N + 15) / 16) <= (int64_t)cu_count();
+    // One wavefront per chunk, except with more than 8 rows in 16-column
+    // workgroups: there each wavefront takes two chunks (at M = 16 measured
+    // 5 % faster on 4096 x 4096 and 9 % on 4096 x 14336).  Which wavefront
+    // computes a chunk changes no bit.
+    int nw = split_k < kFusedMaxWaves ? split_k : kFusedMaxWaves;
+    if (M > 8 && !cols8) nw = split_k / 2 < 1 ? 1 : (split_k / 2 < kFusedMaxWaves ? split_k / 2 : kFusedMaxWaves);
     const dim3 grid((unsigned)(cols8 ? (N + 7) / 8 : (N + 15) / 16)), block(64 * nw);
     const size_t lds = (size_t)split_k * 16 * 16 * sizeof(float);
 #define BI_FUSED(R8, C8)                                                                            \

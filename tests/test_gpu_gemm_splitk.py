@@ -100,13 +100,16 @@ def test_splitk_partials_and_exact_combine(bi):
 
 @pytest.mark.parametrize("M,N,K,S", [(1, 1032, 4096, 32), (16, 1032, 4096, 4), (7, 264, 14336, 8), (5, 520, 3072, 8),
                                      (3, 4096, 2048, 16), (17, 1032, 4096, 32), (32, 264, 14336, 8),
-                                     (25, 520, 3072, 2), (3, 264, 8192, 64), (16, 1032, 16384, 64)])
+                                     (25, 520, 3072, 2), (3, 264, 8192, 64), (16, 1032, 16384, 64),
+                                     (12, 2056, 3840, 3), (9, 4096, 8192, 64)])
 def test_splitk_one_launch_partials_and_fold(bi, M, N, K, S):
     """Batches of at most 16 rows take the one-launch kernel (chunks folded in
     LDS), larger ones the partial and fold kernels.  Either way the workspace
     holds every partial, each matching the oracle over its chunk, and y is
     bit-exactly the oracle's fold of them; N = 1032 and 264 leave the last
-    16-column block half full."""
+    16-column block half full.  Above 8 rows in 16-column workgroups each
+    wavefront takes two or more chunks (split 3: one wavefront takes all
+    three; split 64: sixteen wavefronts take four each)."""
     x = synth.normal_bf16((M, K), 307 + M)
     w = synth.normal_bf16((N, K), 308 + N, std=0.02)
     X, Wt = dev_bf16(x), dev_bf16(w)
