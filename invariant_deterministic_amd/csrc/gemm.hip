@@ -521,8 +521,6 @@ __device__ __forceinline__ void gemm_mainloop2(f32x4 (&acc)[BN / 32][BM / 32], c
 // Stage s of an operand with a ring of D goes into slot s % D as soon as
 // stage s - D is read (after B(s - D + 1); stages 0 .. D - 1 before B(0)):
 // the weights run DW - 1 stages ahead, the activations two.
-// WPE: wavefronts per SIMD the register allocation must allow (4: at most
-// 128 VGPRs, so that two 80 KiB workgroups share a CU).
 template <int BN, int BM, int DW>
 constexpr int role_lds_bytes() {
   return DW * BN * kRow2 + 3 * BM * kRow2;
@@ -636,8 +634,8 @@ __device__ __forceinline__ void role_tile(char *lds, const uint16_t *__restrict_
   store_tile<BN, BM>(acc, lds, y, M, N, ldy, m0, n0, wn, wm, wv, lane);
 }
 
-template <int BN, int BM, int WPE, int DW>
-__global__ __launch_bounds__(2 * kThreads, WPE) void gemm_split_role_kernel(
+template <int BN, int BM, int DW>
+__global__ __launch_bounds__(2 * kThreads, 1) void gemm_split_role_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
     int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) char lds[role_lds_bytes<BN, BM, DW>()];
@@ -1069,9 +1067,9 @@ struct CfgEntry {
 // as configuration 0.
 const CfgEntry kConfigs[] = {
     {256, 256, gemm_kernel<256, 256>, gemm_pp_kernel<256, 256>, 512, false},
-    {256, 128, gemm_kernel<256, 128>, gemm_split_role_kernel<256, 128, 1, 2>, 2 * kThreads, false},
-    {128, 128, gemm_kernel<128, 128>, gemm_split_role_kernel<128, 128, 1, 3>, 2 * kThreads, false},
-    {128, 256, gemm_kernel<128, 256>, gemm_split_role_kernel<128, 256, 1, 2>, 2 * kThreads, false},
+    {256, 128, gemm_kernel<256, 128>, gemm_split_role_kernel<256, 128, 2>, 2 * kThreads, false},
+    {128, 128, gemm_kernel<128, 128>, gemm_split_role_kernel<128, 128, 3>, 2 * kThreads, false},
+    {128, 256, gemm_kernel<128, 256>, gemm_split_role_kernel<128, 256, 2>, 2 * kThreads, false},
     {256, 256, gemm_kernel<256, 256>, gemm_mixed_kernel, 512, true},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
