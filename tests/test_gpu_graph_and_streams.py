@@ -195,3 +195,36 @@ def test_graph_replays_split_k_both_launch_forms(bi):
         for X, *_ in cases:                        # eager work between replays
             bi.bi_gemm_splitk(X, W, split_k=S)
         torch.cuda.synchronize()
+
+
+def test_graph_replays_fill_mixed_launch(bi):
+    """bi_gemm_fill at a shape where it takes the mixed launch (272 tiles of
+    256 x 256: each XCD's last two run as 256 x 128 halves), captured in a
+    graph: every replay, with eager work in between, reproduces the eager
+    bits, which are bi_gemm's."""
+    M, N, K = 4200, 4096, 256
+    mixed = bi.bi_gemm_num_configs() - 1
+    assert bi.bi_gemm_fill_config_id(M, N, K) == mixed
+    X = dev_bf16(synth.normal_bf16((M, K), 9101))
+    W = dev_bf16(synth.normal_bf16((N, K), 9102, std=0.02))
+    ref = bi.bi_gemm(X, W)
+    out = torch.empty_like(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bi.bi_gemm_fill(X, W, y=out)             # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        bi.bi_gemm_fill(X, W, y=out)
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"graph replay of the mixed fill launch {rep}")
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+        bi.bi_gemm(X, W)                          # eager work between replays
+        torch.cuda.synchronize()
