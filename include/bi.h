@@ -154,8 +154,9 @@ int bi_gemm_launch_plan(int64_t M, int64_t N, int64_t K, int64_t *plan);
  * (0 <= config < bi_gemm_num_configs()) instead of bi_gemm_config_id(N, K).
  * Every configuration runs the same reduction order, so all of them return the
  * same bits; this entry point exists to demonstrate exactly that and to time
- * the alternatives.  Configurations 0-3 are single tiles (256 x 256,
- * 256 x 128, 128 x 128, 128 x 256 outputs of w rows x x rows per workgroup);
+ * the alternatives.  Configurations 0-4 are single tiles (256 x 256,
+ * 256 x 128, 128 x 128, 128 x 256, 128 x 64 outputs of w rows x x rows per
+ * workgroup);
  * the last one is a mixed launch of 256 x 256 tiles whose last wave on each
  * XCD, when it is at most half full, runs as 256 x 128 halves (with K % 64 ==
  * 32 it runs as configuration 0).  Same arguments and errors as bi_gemm, plus

@@ -644,6 +644,18 @@ __global__ __launch_bounds__(2 * kThreads, 1) void gemm_split_role_kernel(
   role_tile<BN, BM, DW>(lds, x, w, y, M, N, K, ldx, ldw, ldy, tm, tn);
 }
 
+// The same tile bounded to 128 registers per lane, so that two workgroups
+// share a CU when their LDS fits twice (the 128 x 64 tile: 72 KiB).
+template <int BN, int BM, int DW>
+__global__ __launch_bounds__(2 * kThreads, 4) void gemm_split_role_pair_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
+    int M, int N, int K, int64_t ldx, int64_t ldw, int64_t ldy, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char lds[role_lds_bytes<BN, BM, DW>()];
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  role_tile<BN, BM, DW>(lds, x, w, y, M, N, K, ldx, ldw, ldy, tm, tn);
+}
+
 template <int BN, int BM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, uint16_t *__restrict__ y,
@@ -1062,6 +1074,11 @@ struct CfgEntry {
 // doing both, 8-9 % at 256 x 128).  At 128 x 128 the weights take a ring of 3
 // too (96 KiB, one workgroup per CU): 11-20 % faster at M <= 4096 than the
 // ring of 2 with two workgroups per CU, 8 % slower at M = 8192.
+// The 128 x 64 tile runs two workgroups per CU (72 KiB of LDS, 92 registers);
+// only bi_gemm_fill picks it, where 128 x 128 tiles would leave at least half
+// of the CUs idle: on N = 1024, K = 4096 it measured 434 / 795 TFLOP/s at
+// M = 1024 / 2048 against 353 / 701 for 128 x 128, and 868 against 1110 at
+// M = 4096.
 // The last configuration is the mixed 256 x 256 / 256 x 128 launch: only
 // bi_gemm_fill picks it (the split follows M), and with K % 64 == 32 it runs
 // as configuration 0.
@@ -1070,6 +1087,7 @@ const CfgEntry kConfigs[] = {
     {256, 128, gemm_kernel<256, 128>, gemm_split_role_kernel<256, 128, 2>, 2 * kThreads, false},
     {128, 128, gemm_kernel<128, 128>, gemm_split_role_kernel<128, 128, 3>, 2 * kThreads, false},
     {128, 256, gemm_kernel<128, 256>, gemm_split_role_kernel<128, 256, 2>, 2 * kThreads, false},
+    {128, 64, gemm_kernel<128, 64>, gemm_split_role_pair_kernel<128, 64, 3>, 2 * kThreads, false},
     {256, 256, gemm_kernel<256, 256>, gemm_mixed_kernel, 512, true},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
@@ -1097,14 +1115,16 @@ int config_for(int64_t N, int64_t K) {
 // Tile for bi_gemm_fill: the configuration with the smallest estimated time,
 // (waves of tiles over the CUs) x (relative time of one tile).  The tile
 // costs are measured ones, relative to 256 x 256: a 256 x 128 tile takes
-// ~0.68 of it, a 128 x 256 tile ~0.67, a 128 x 128 tile ~0.34 (so three
-// waves of either half-size tile do not replace two of the big tile, which
-// measured 1-9 % slower).  The mixed launch costs each XCD its full waves of
+// ~0.68 of it, a 128 x 256 tile ~0.67, a 128 x 128 tile ~0.34 and a 128 x 64
+// tile ~0.23 (a wave is one tile per CU).  So three waves of either half-size
+// tile do not replace two of the big tile (measured 1-9 % slower), and the
+// 128 x 64 tile wins only where it fills the chip in one wave and 128 x 128
+// tiles fill at most half of it.  The mixed launch costs each XCD its full waves of
 // 256 x 256 tiles plus, if it cuts a tail, one wave of 256 x 128 tiles; it is
 // taken only for 64-k stages on a chip of 8 x kCusPerXcd CUs.  Ties keep the
 // earlier configuration.
 int fill_config_for(int64_t M, int64_t N, int64_t K) {
-  static const double kTileCost[kNumConfigs] = {1.0, 0.68, 0.34, 0.67, 1.0};
+  static const double kTileCost[kNumConfigs] = {1.0, 0.68, 0.34, 0.67, 0.23, 1.0};
   const int64_t cus = cu_count();
   int best = 0;
   double best_t = 0.0;

@@ -190,10 +190,14 @@ def test_gemm_fill_validation_and_choice(lib):
     if c(4096, 4096, 4096) == 0:
         assert c(2048, 4096, 4096) == 3 and c(1000, 4096, 4096) == 2
         # 256 x 256 tiles with each XCD's tail of at most half a wave cut into
-        # 256 x 128 halves (4): 896, 560, 272 and 2688 tiles leave 16, 6, 2 and
+        # 256 x 128 halves (5): 896, 560, 272 and 2688 tiles leave 16, 6, 2 and
         # 16 on each XCD after its full waves
-        assert c(4096, 14336, 4096) == 4 and c(2305, 14336, 4096) == 4
-        assert c(4200, 4096, 4096) == 4 and c(6144, 28672, 8192) == 4
+        assert c(4096, 14336, 4096) == 5 and c(2305, 14336, 4096) == 5
+        assert c(4200, 4096, 4096) == 5 and c(6144, 28672, 8192) == 5
+        # 128 x 64 tiles (4) only where 128 x 128 tiles fill at most half the
+        # CUs and 128 x 64 tiles fill them in one wave
+        assert c(2048, 1024, 4096) == 4 and c(1024, 1024, 4096) == 4
+        assert c(512, 4096, 4096) == 4 and c(3072, 1024, 4096) == 2
         # whole waves (1792 tiles) or a tail of more than half a wave (448
         # tiles: 24 per XCD): the big tile alone
         assert c(8192, 14336, 4096) == 0 and c(2048, 14336, 4096) == 0
