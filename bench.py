@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--M", type=int, default=4096)
     ap.add_argument("--sweep", default=None)
     ap.add_argument("--only", default=None,
-                    choices=["gemm", "gemm_kv", "gemm_up", "gemm_up_fill", "gemm_down", "rmsnorm", "shrink_det8",
+                    choices=["gemm", "gemm_kv", "gemm_kv_fill", "gemm_up", "gemm_up_fill", "gemm_down", "rmsnorm", "shrink_det8",
                              "shrink_two_pass", "shrink_atomic8", "shrink_unsplit", "copy",
                              "splitk", "attention", "expand"])
     ap.add_argument("--iters", type=int, default=50, help="launches for --only")
@@ -973,6 +973,7 @@ def run_only(args, bi, torch, dev, X, G, H, Wq, Wkv, Wup, Wdown, U, A, L, WS, La
     else:
         launch = {"gemm": lambda i: bi.bi_gemm(H, Wq, y=Q),
                   "gemm_kv": lambda i: bi.bi_gemm(H, Wkv, y=KV),
+                  "gemm_kv_fill": lambda i: bi.bi_gemm_fill(H, Wkv, y=KV),
                   "gemm_up": lambda i: bi.bi_gemm(H, Wup, y=U2),
                   "gemm_up_fill": lambda i: bi.bi_gemm_fill(H, Wup, y=U2),
                   "gemm_down": lambda i: bi.bi_gemm(U, Wdown, y=D)}[args.only]
