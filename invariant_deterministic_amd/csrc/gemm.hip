@@ -1321,14 +1321,25 @@ int splitk_launch(const uint16_t *x, const uint16_t *w, uint16_t *y, int64_t M, 
 #undef BI_FUSED
     return launch_status();
   }
-  if (kc % BK2 == 0)
-    hipLaunchKernelGGL((gemm_partial_kernel<kSplitBN, kSplitBM, true>),
-                       dim3((unsigned)(tiles_m * tiles_n), (unsigned)split_k), dim3(kThreads), 0, s,
-                       x, w, wsf, (int)M, (int)N, kc, ldx, ldw, (int)tiles_m, (int)tiles_n);
-  else
-    hipLaunchKernelGGL((gemm_partial_kernel<kSplitBN, kSplitBM, false>),
-                       dim3((unsigned)(tiles_m * tiles_n), (unsigned)split_k), dim3(kThreads), 0, s,
-                       x, w, wsf, (int)M, (int)N, kc, ldx, ldw, (int)tiles_m, (int)tiles_n);
+  // 64-column partial tiles when 128-column ones would leave at least half of
+  // the CUs idle (N = 1024 at M <= 64: 256 workgroups instead of 128).  Every
+  // partial is the same ascending run of 32-k steps whatever the tile, so the
+  // bits do not change.
+  const bool narrow = 2 * tiles_m * tiles_n * split_k <= (int64_t)cu_count();
+  constexpr int kNarrowBN = kSplitBN / 2;
+  const int64_t pt_n = narrow ? (N + kNarrowBN - 1) / kNarrowBN : tiles_n;  // partial tile columns
+#define BI_PARTIAL(BN, WIDE)                                                                       \
+  hipLaunchKernelGGL((gemm_partial_kernel<BN, kSplitBM, WIDE>),                                    \
+                     dim3((unsigned)(tiles_m * pt_n), (unsigned)split_k), dim3(kThreads), 0, s, x, \
+                     w, wsf, (int)M, (int)N, kc, ldx, ldw, (int)tiles_m, (int)pt_n)
+  if (kc % BK2 == 0) {
+    if (narrow) BI_PARTIAL(kNarrowBN, true);
+    else BI_PARTIAL(kSplitBN, true);
+  } else {
+    if (narrow) BI_PARTIAL(kNarrowBN, false);
+    else BI_PARTIAL(kSplitBN, false);
+  }
+#undef BI_PARTIAL
   int st = launch_status();
   if (st != BI_OK) return st;
   const int64_t groups = (M * N / 4 + kThreads - 1) / kThreads;
