@@ -1119,10 +1119,10 @@ int config_for(int64_t N, int64_t K) {
 // tile ~0.23 (a wave is one tile per CU).  So three waves of either half-size
 // tile do not replace two of the big tile (measured 1-9 % slower), and the
 // 128 x 64 tile wins only where it fills the chip in one wave and 128 x 128
-// tiles fill at most half of it.  The mixed launch costs each XCD its full waves of
-// 256 x 256 tiles plus, if it cuts a tail, one wave of 256 x 128 tiles; it is
-// taken only for 64-k stages on a chip of 8 x kCusPerXcd CUs.  Ties keep the
-// earlier configuration.
+// tiles fill at most half of it.  The mixed launch costs each XCD its full
+// waves of 256 x 256 tiles plus, if it cuts a tail, one wave of 256 x 128
+// tiles; it is taken only for 64-k stages on a chip of 8 x kCusPerXcd CUs.
+// Ties keep the earlier configuration.
 int fill_config_for(int64_t M, int64_t N, int64_t K) {
   static const double kTileCost[kNumConfigs] = {1.0, 0.68, 0.34, 0.67, 0.23, 1.0};
   const int64_t cus = cu_count();
