@@ -198,6 +198,8 @@ def test_gemm_fill_validation_and_choice(lib):
         # CUs and 128 x 64 tiles fill them in one wave
         assert c(2048, 1024, 4096) == 4 and c(1024, 1024, 4096) == 4
         assert c(512, 4096, 4096) == 4 and c(3072, 1024, 4096) == 2
+        # never for more tiles than CUs: Up at M = 520 would need four waves
+        assert c(520, 14336, 4096) == 0 and c(576, 14336, 4096) == 0
         # whole waves (1792 tiles) or a tail of more than half a wave (448
         # tiles: 24 per XCD): the big tile alone
         assert c(8192, 14336, 4096) == 0 and c(2048, 14336, 4096) == 0
